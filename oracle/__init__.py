@@ -1,0 +1,165 @@
+"""CPU oracle for the row top-K select and the candidate merge.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package; the library in
+``row_top_select_amd`` never does, and the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, qsort-based, see its header for
+the passages each function follows).  This module only compiles it with gcc
+when the shared object is missing or stale and marshals numpy arrays.
+
+Parity pins for every function are in ``tests/test_oracle_*.py``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` (gcc, OpenMP over rows)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+             "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+            lib.oracle_topk_rows.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, i64,
+                                             ctypes.c_int]
+            lib.oracle_pack_candidates.argtypes = [p, i64, i64, i64, p, i32, i64, p, p]
+            lib.oracle_merge_select_rank_major.argtypes = [p, i32, i64, i32, i32, p, p]
+            lib.oracle_pack_pairs.argtypes = [p, i64, i64, i64, p, i32, i64, p, i32, i32, p]
+            lib.oracle_merge_select_pairs_rank_major.argtypes = [p, i32, i64, i32, i32, p]
+            for f in (lib.oracle_topk_rows, lib.oracle_pack_candidates,
+                      lib.oracle_merge_select_rank_major, lib.oracle_pack_pairs,
+                      lib.oracle_merge_select_pairs_rank_major):
+                f.restype = ctypes.c_int
+            lib.oracle_max_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name}: invalid arguments (rc={rc})")
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def topk_rows(x, row_ends, k, out=None, nthreads=0):
+    """Exact per-row top-k ids of ``x`` (fp32 ndarray, or bf16 bits as uint16).
+
+    ``row_ends`` is int32 [rows] or None (all rows full).  Returns int32
+    [rows, k] (or fills ``out``, whose columns past k are left untouched).
+    """
+    lib = _load()
+    if k < 1:
+        raise ValueError("k must be >= 1")
+    x = np.asarray(x)
+    if x.dtype == np.float32:
+        dt = 0
+    elif x.dtype == np.uint16:
+        dt = 1
+    else:
+        raise TypeError("x must be float32 or uint16 (bf16 bits)")
+    if x.ndim != 2 or x.strides[1] != x.itemsize or x.strides[0] % x.itemsize:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    ld = x.strides[0] // x.itemsize if rows > 1 else cols
+    if row_ends is not None:
+        row_ends = np.ascontiguousarray(row_ends, dtype=np.int32)
+        assert row_ends.shape == (rows,)
+    if out is None:
+        out = np.empty((rows, k), dtype=np.int32)
+    assert out.dtype == np.int32 and out.ndim == 2 and out.strides[1] == 4
+    ld_out = out.strides[0] // 4 if rows > 1 else k
+    _check(lib.oracle_topk_rows(_ptr(x), dt, rows, cols, ld, _ptr(row_ends), k, _ptr(out),
+                                ld_out, nthreads), "topk_rows")
+    return out
+
+
+def pack_candidates(x_bf16, local_idx, row_ends=None):
+    """B' packed rows int32 [rows, n + n/32] of a local top-n (``local_idx``)."""
+    lib = _load()
+    x = np.asarray(x_bf16)
+    assert x.dtype == np.uint16 and x.ndim == 2 and x.strides[1] == 2
+    local_idx = np.ascontiguousarray(local_idx, dtype=np.int32)
+    rows, cols = x.shape
+    n = local_idx.shape[1]
+    if row_ends is not None:
+        row_ends = np.ascontiguousarray(row_ends, dtype=np.int32)
+    packed = np.empty((rows, n + n // 32), dtype=np.int32)
+    ld = x.strides[0] // 2 if rows > 1 else cols
+    _check(lib.oracle_pack_candidates(_ptr(x), rows, cols, ld, _ptr(local_idx), n, n,
+                                      _ptr(row_ends), _ptr(packed)), "pack_candidates")
+    return packed
+
+
+def merge_select_rank_major(gathered, k, with_sat=True):
+    """Select from int32 [W, R, n + n/32]; returns (ids [R, k], sat_word [R] or None)."""
+    lib = _load()
+    g = np.ascontiguousarray(gathered, dtype=np.int32)
+    world, rows, width = g.shape
+    n = width * 32 // 33
+    assert n + n // 32 == width
+    ids = np.empty((rows, k), dtype=np.int32)
+    sat = np.empty((rows,), dtype=np.int32) if with_sat else None
+    _check(lib.oracle_merge_select_rank_major(_ptr(g), world, rows, n, k, _ptr(ids), _ptr(sat)),
+           "merge_select_rank_major")
+    return ids, sat
+
+
+def pack_pairs(x, local_idx, rank, world, row_ends=None):
+    """(score bits, gid) pairs int32 [rows, kc, 2] of a local top-kc of fp32 ``x``."""
+    lib = _load()
+    x = np.asarray(x)
+    assert x.dtype == np.float32 and x.ndim == 2 and x.strides[1] == 4
+    local_idx = np.ascontiguousarray(local_idx, dtype=np.int32)
+    rows, cols = x.shape
+    kc = local_idx.shape[1]
+    if row_ends is not None:
+        row_ends = np.ascontiguousarray(row_ends, dtype=np.int32)
+    pairs = np.empty((rows, kc, 2), dtype=np.int32)
+    ld = x.strides[0] // 4 if rows > 1 else cols
+    _check(lib.oracle_pack_pairs(_ptr(x), rows, cols, ld, _ptr(local_idx), kc, kc,
+                                 _ptr(row_ends), rank, world, _ptr(pairs)), "pack_pairs")
+    return pairs
+
+
+def merge_select_pairs_rank_major(pairs, k):
+    """Select from int32 [W, R, kc, 2]; returns ids [R, k]."""
+    lib = _load()
+    p = np.ascontiguousarray(pairs, dtype=np.int32)
+    world, rows, kc, two = p.shape
+    assert two == 2
+    ids = np.empty((rows, k), dtype=np.int32)
+    _check(lib.oracle_merge_select_pairs_rank_major(_ptr(p), world, rows, kc, k, _ptr(ids)),
+           "merge_select_pairs_rank_major")
+    return ids

@@ -1,0 +1,100 @@
+"""Pure-Python brute force for tiny inputs, written independently of oracle/.
+
+Each function restates a definition from the pages with Python tuple sorts and
+explicit loops; the oracle tests compare the C oracle against these.
+"""
+
+import math
+import struct
+
+
+def f32_of_bits(u):
+    return struct.unpack("<f", struct.pack("<I", u & 0xFFFFFFFF))[0]
+
+
+def bits_of_f32(v):
+    return struct.unpack("<I", struct.pack("<f", v))[0]
+
+
+def bf16_value(b):
+    return f32_of_bits((b & 0xFFFF) << 16)
+
+
+def order_key(v, ident):
+    """Sort key for (score desc, -0 below +0, id asc)."""
+    return (-v, 1 if math.copysign(1.0, v) < 0 and v == 0 else 0, ident)
+
+
+def topk_row(values, end, k):
+    """values: list of Python floats (NaN allowed); returns k ids (-1 padded)."""
+    e = max(0, min(end, len(values)))
+    cands = [(order_key(values[j], j), j) for j in range(e) if not math.isnan(values[j])]
+    cands.sort()
+    ids = [j for _, j in cands[:k]]
+    return ids + [-1] * (k - len(ids))
+
+
+def ord16(b):
+    b &= 0xFFFF
+    return (~b & 0xFFFF) if b & 0x8000 else (b | 0x8000)
+
+
+def pack_row(bf16_row, local_ids, end, n):
+    """One B' row (n words + n/32 plane words) as Python ints (uint32 values)."""
+    lim = min(end, len(bf16_row), 1 << 17)
+    words = [0] * n
+    plane = [0] * (n // 32)
+    for j in range(n):
+        loc = local_ids[j]
+        if 0 <= loc < lim:
+            b = bf16_row[loc]
+            if (b & 0x7FFF) <= 0x7F80:
+                words[j] = (ord16(b) << 16) | (0xFFFF - (loc & 0xFFFF))
+                if (loc >> 16) & 1:
+                    plane[j // 32] |= 1 << (j % 32)
+    return words + plane
+
+
+def merge_row(gathered_row, world, n, k):
+    """gathered_row[r] = list of n + n/32 uint32 words of rank r for one row.
+
+    Returns (ids in candidate order + -1 tail, sat_word as uint32)."""
+    cands = []
+    for r in range(world):
+        row = gathered_row[r]
+        for j in range(n):
+            w = row[j] & 0xFFFFFFFF
+            if w == 0:
+                continue
+            hi = (row[n + j // 32] >> (j % 32)) & 1
+            local = (0xFFFF - (w & 0xFFFF)) | (hi << 16)
+            gid = local * world + r
+            cands.append(((-(w >> 16), gid, r * n + j), gid, w >> 16, r * n + j))
+    cands.sort()
+    chosen = cands[:k]
+    tau = chosen[-1][2] if len(cands) >= k else 0
+    by_pos = sorted((pos, gid) for _, gid, _, pos in chosen)
+    ids = [gid for _, gid in by_pos] + [-1] * (k - len(chosen))
+    mask = 0
+    for r in range(world):
+        row = gathered_row[r]
+        if all((row[j] & 0xFFFFFFFF) != 0 and ((row[j] & 0xFFFFFFFF) >> 16) > tau for j in range(n)):
+            mask |= 1 << r
+    if bin(mask).count("1") > (k - 1) // n:
+        mask = 0
+    return ids, ((mask << 16) | tau) & 0xFFFFFFFF
+
+
+def merge_pairs_row(pairs_row, world, kc, k):
+    """pairs_row[r][j] = (score bits, gid).  Returns ids in candidate order + -1 tail."""
+    cands = []
+    for r in range(world):
+        for j in range(kc):
+            sbits, gid = pairs_row[r][j]
+            v = f32_of_bits(sbits)
+            if gid < 0 or math.isnan(v):
+                continue
+            cands.append((order_key(v, gid) + (r * kc + j,), gid, r * kc + j))
+    cands.sort()
+    chosen = sorted((pos, gid) for _, gid, pos in cands[:k])
+    return [gid for _, gid in chosen] + [-1] * (k - len(chosen))

@@ -1,0 +1,345 @@
+"""Pins of the oracle's pack / merge / pair functions to facts outside them.
+
+* golden words and merges derived by hand (tests/golden/*.json);
+* the order-preserving bf16 key checked exhaustively over all 65536 patterns
+  against float comparison (the defining property on the kernels page);
+* pure-Python brute force (tests/brute.py) on tiny W / R / N;
+* the pages' exactness claims as invariants: the merged score multiset equals
+  the top-K of the union of all ranks' scores (numpy sort of the global row),
+  and with an empty saturation mask the ids equal the direct top-K;
+* the producer contract of assert_packed_merge_contract (count, distinct ids
+  below the row end, word score = logit bits, no unsent token above a sent one);
+* the pair identity: selecting from W local top-K lists equals the top-K of
+  the union.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import brute
+import datagen
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _h(s):
+    return int(s, 16)
+
+
+def test_golden_pack_words():
+    g = json.load(open(os.path.join(GOLDEN, "pack_words.json")))
+    cases = g["cases"]
+    n = 32
+    cols = 1 << 17
+    x = np.zeros((len(cases), cols), np.uint16)
+    idx = np.full((len(cases), n), -1, np.int32)
+    for t, c in enumerate(cases):
+        x[t, c["local"]] = _h(c["bf16"])
+        idx[t, 7] = c["local"]          # slot 7
+    p = oracle.pack_candidates(x, idx).view(np.uint32)
+    for t, c in enumerate(cases):
+        assert p[t, 7] == _h(c["word"]), c["why"]
+        assert ((p[t, n] >> 7) & 1) == c["plane_bit"], c["why"]
+        others = np.delete(p[t, :n], 7)
+        assert (others == 0).all()
+
+
+def test_ord16_is_order_preserving_exhaustive():
+    # Every bf16 pattern at its own local id; one row of 65536 slots.
+    n = 65536
+    b = np.arange(n, dtype=np.uint32).astype(np.uint16)
+    x = b[None]
+    idx = np.arange(n, dtype=np.int32)[None]
+    words = oracle.pack_candidates(x, idx)[0, :n].view(np.uint32)
+    vals = datagen.bf16_to_f32(b)
+    nan = np.isnan(vals)
+    assert (words[nan] == 0).all()
+    assert (words[~nan] != 0).all()
+    key = words >> 16
+    # Order of the keys == order of the values with -0 below +0.
+    v = vals[~nan].astype(np.float64)
+    v = np.where((v == 0) & np.signbit(v), -1e-300, v)   # -0 just below +0
+    order = np.argsort(v, kind="stable")
+    ks = key[~nan][order]
+    vs = v[order]
+    assert (np.diff(ks.astype(np.int64)) >= 0).all()
+    same_val = np.diff(vs) == 0
+    assert ((np.diff(ks.astype(np.int64)) == 0) == same_val).all()
+    # low half is 0xFFFF - local
+    assert (words[~nan] & 0xFFFF == (0xFFFF - np.arange(n))[~nan]).all()
+
+
+def test_pack_drop_rules():
+    cols = 40
+    x = np.full((3, cols), 0x3F80, np.uint16)
+    x[:, 5] = 0x7FC1            # NaN
+    idx = np.full((3, 32), -1, np.int32)
+    idx[:, 0] = 3
+    idx[:, 1] = 5               # NaN score
+    idx[:, 2] = 20              # at/after the row end of row 1
+    idx[:, 3] = cols            # past the row
+    idx[:, 4] = -7
+    ends = np.array([cols, 20, 0], np.int32)
+    p = oracle.pack_candidates(x, idx, ends).view(np.uint32)
+    assert p[0, 0] == 0xBF80FFFC and p[0, 2] != 0
+    assert p[1, 0] != 0 and p[1, 2] == 0
+    assert (p[2, :32] == 0).all()
+    assert (p[:, 1] == 0).all() and (p[:, 3] == 0).all() and (p[:, 4] == 0).all()
+
+
+def test_pack_local_index_limit():
+    # ids at or past 2**17 cannot be encoded and pack as empty
+    cols = (1 << 17) + 64
+    x = np.full((1, cols), 0x3F80, np.uint16)
+    idx = np.full((1, 32), -1, np.int32)
+    idx[0, 0] = (1 << 17) - 1
+    idx[0, 1] = 1 << 17
+    p = oracle.pack_candidates(x, idx).view(np.uint32)
+    assert p[0, 0] != 0 and p[0, 1] == 0
+
+
+def test_pack_brute_force():
+    rng = np.random.default_rng(21)
+    for trial in range(20):
+        rows, cols, n = 4, int(rng.integers(1, 200)), 32 * int(rng.integers(1, 4))
+        x = datagen.bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32))
+        x[rng.random((rows, cols)) < 0.05] = 0x7FC0
+        idx = rng.integers(-2, cols + 3, size=(rows, n)).astype(np.int32)
+        ends = rng.integers(-1, cols + 2, size=rows).astype(np.int32)
+        got = oracle.pack_candidates(x, idx, ends).view(np.uint32)
+        for t in range(rows):
+            exp = brute.pack_row(x[t].tolist(), idx[t].tolist(), int(ends[t]), n)
+            assert got[t].tolist() == exp, (trial, t)
+
+
+def _gathered_from_fill(fill, world, n):
+    g = np.zeros((world, 1, n + n // 32), np.int32)
+    if fill == "small":
+        small = {0: [(0x3F80, 0), (0x4000, 3)], 1: [(0x4000, 1), (0x3F00, 2)]}
+        for r, lst in small.items():
+            for j, (b, loc) in enumerate(lst):
+                g[r, 0, j] = np.uint32((brute.ord16(b) << 16) | (0xFFFF - loc)).view(np.int32)
+    else:
+        for r, b in ((0, 0x4080), (1, 0x3F80)):
+            for j in range(n):
+                g[r, 0, j] = np.uint32((brute.ord16(b) << 16) | (0xFFFF - j)).view(np.int32)
+    return g
+
+
+def test_golden_merge():
+    gd = json.load(open(os.path.join(GOLDEN, "merge_small.json")))
+    world, n = gd["world"], gd["n"]
+    for c in gd["cases"]:
+        g = _gathered_from_fill(c["fill"], world, n)
+        ids, sat = oracle.merge_select_rank_major(g, c["k"])
+        assert np.uint32(sat[0].view(np.uint32)) == _h(c["sat_word"]), c["why"]
+        if "expected_ids" in c:
+            assert ids[0].tolist() == c["expected_ids"], c["why"]
+        if "expected_ids_prefix" in c:
+            pre = c["expected_ids_prefix"]
+            assert ids[0, :len(pre)].tolist() == pre
+            assert (ids[0, len(pre):] == -1).all()
+        if c["fill"] == "saturate":
+            exp = [2 * j for j in range(n)] + [2 * j + 1 for j in range(8)]
+            assert ids[0].tolist() == exp
+
+
+def _random_gathered(rng, world, rows, n, fill_prob=0.9, dup=False):
+    g = np.zeros((world, rows, n + n // 32), np.uint32)
+    for r in range(world):
+        for t in range(rows):
+            locs = rng.choice(1 << 17, size=n, replace=dup)
+            scores = datagen.bf16_bits(rng.standard_normal(n).astype(np.float32) * 2)
+            if rng.random() < 0.3:
+                scores = (rng.integers(0, 4, size=n) + 0x3F80).astype(np.uint16)   # ties
+            for j in range(n):
+                if rng.random() < fill_prob:
+                    g[r, t, j] = (brute.ord16(int(scores[j])) << 16) | (0xFFFF - (int(locs[j]) & 0xFFFF))
+                    if (locs[j] >> 16) & 1:
+                        g[r, t, n + j // 32] |= np.uint32(1 << (j % 32))
+    return g.view(np.int32)
+
+
+@pytest.mark.parametrize("world,n,k", [(2, 32, 5), (3, 32, 40), (4, 64, 100), (1, 32, 32), (5, 32, 200)])
+def test_merge_brute_force(world, n, k):
+    rng = np.random.default_rng(world * 100 + n + k)
+    rows = 6
+    g = _random_gathered(rng, world, rows, n, fill_prob=0.85 if k != 32 else 1.0)
+    ids, sat = oracle.merge_select_rank_major(g, k)
+    gu = g.view(np.uint32)
+    for t in range(rows):
+        exp_ids, exp_sat = brute.merge_row([gu[r, t].tolist() for r in range(world)], world, n, k)
+        assert ids[t].tolist() == exp_ids, t
+        assert int(sat[t].view(np.uint32)) == exp_sat, t
+
+
+def test_mask_never_exceeds_slots():
+    # (K-1)//N bounds the saturated ranks for any input, duplicates included.
+    rng = np.random.default_rng(77)
+    for trial in range(20):
+        world, n = int(rng.integers(1, 6)), 32
+        k = int(rng.integers(1, world * n + 40))
+        g = _random_gathered(rng, world, 3, n, fill_prob=1.0, dup=bool(trial % 2))
+        _, sat = oracle.merge_select_rank_major(g, k)
+        for s in sat.view(np.uint32):
+            assert bin(int(s) >> 16).count("1") <= (k - 1) // n
+
+
+def _global_bf16(rows, world, s, seed):
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((rows, world * s)).astype(np.float32)
+    return datagen.bf16_bits(g)
+
+
+@pytest.mark.parametrize("world,s,n,k,some_exact",
+                         [(8, 1024, 96, 512, True), (4, 2048, 256, 512, True),
+                          (8, 512, 64, 512, False)])
+def test_merge_exactness_invariants(world, s, n, k, some_exact):
+    # Round 1 is exact when the saturation mask is 0; otherwise it can only miss
+    # tokens of saturated ranks (those scoring above tau; equal scores may go
+    # either way).
+    rows = 24
+    gb = _global_bf16(rows, world, s, seed=world + s + n)
+    ranks = datagen.rank_slices(gb, world)                 # [W, R, S]
+    packed = np.stack([oracle.pack_candidates(ranks[r], oracle.topk_rows(ranks[r], None, n))
+                       for r in range(world)])
+    oracle_ids, sat = oracle.merge_select_rank_major(packed, k)
+    vals = datagen.bf16_to_f32(gb)
+    n_zero_mask = 0
+    for t in range(rows):
+        ids = oracle_ids[t]
+        assert (ids >= 0).all() and len(set(ids.tolist())) == k
+        sw = int(sat[t].view(np.uint32))
+        mask, tau = sw >> 16, sw & 0xFFFF
+        assert tau == brute.ord16(int(gb[t, ids[np.argmin(vals[t, ids])]]))
+        direct = np.lexsort((np.arange(world * s), -vals[t].astype(np.float64)))[:k]
+        if mask == 0:
+            n_zero_mask += 1
+            # merged score multiset == top-k of the union, ids == direct top-k
+            assert np.array_equal(np.sort(vals[t, ids]), np.sort(vals[t])[-k:])
+            assert set(ids.tolist()) == set(direct.tolist())
+        else:
+            tau_val = vals[t, ids].min()
+            missing = set(direct.tolist()) - set(ids.tolist())
+            for gid in missing:
+                if vals[t, gid] > tau_val:
+                    assert (mask >> (gid % world)) & 1, (t, gid)
+    assert (n_zero_mask > 0) == some_exact
+
+
+def test_saturated_rank_detected():
+    # One rank holds every top score: it sends N words all above tau, so its bit is set.
+    world, s, n, k = 4, 512, 64, 200
+    rng = np.random.default_rng(4)
+    g = rng.standard_normal((2, world * s)).astype(np.float32)
+    g[:, 1::world] += 10.0                                   # rank 1 owns the top scores
+    gb = datagen.bf16_bits(g)
+    ranks = datagen.rank_slices(gb, world)
+    packed = np.stack([oracle.pack_candidates(ranks[r], oracle.topk_rows(ranks[r], None, n))
+                       for r in range(world)])
+    _, sat = oracle.merge_select_rank_major(packed, k)
+    for sw in sat.view(np.uint32):
+        assert (int(sw) >> 16) == 0b0010
+
+
+def test_fewer_than_k_candidates():
+    world, n, k = 2, 32, 512
+    g = _random_gathered(np.random.default_rng(8), world, 3, n, fill_prob=0.5)
+    ids, sat = oracle.merge_select_rank_major(g, k)
+    for t in range(3):
+        cnt = int((g[:, t, :n] != 0).sum())
+        assert (ids[t, :cnt] >= 0).all() and (ids[t, cnt:] == -1).all()
+        assert (int(sat[t].view(np.uint32)) & 0xFFFF) == 0
+
+
+def test_golden_pairs():
+    gd = json.load(open(os.path.join(GOLDEN, "pairs_small.json")))
+    world, kc = gd["world"], gd["kc"]
+    p = np.zeros((world, 1, kc, 2), np.int32)
+    for r in range(world):
+        for j, (s, gid) in enumerate(gd["pairs"][r]):
+            p[r, 0, j, 0] = np.float32(float(s)).view(np.int32)
+            p[r, 0, j, 1] = gid
+    for c in gd["cases"]:
+        assert oracle.merge_select_pairs_rank_major(p, c["k"])[0].tolist() == c["expected"], c["why"]
+
+
+def test_pairs_brute_force():
+    rng = np.random.default_rng(31)
+    for trial in range(15):
+        world, rows, kc = int(rng.integers(1, 5)), 3, int(rng.integers(1, 40))
+        k = int(rng.integers(1, world * kc + 5))
+        p = np.zeros((world, rows, kc, 2), np.int32)
+        v = rng.integers(-3, 4, size=(world, rows, kc)).astype(np.float32)
+        v[rng.random(v.shape) < 0.05] = np.nan
+        v[rng.random(v.shape) < 0.05] = -0.0
+        p[..., 0] = v.view(np.int32)
+        p[..., 1] = rng.permutation(world * rows * kc * 3)[:world * rows * kc].reshape(world, rows, kc)
+        p[..., 1][rng.random(v.shape) < 0.1] = -1
+        got = oracle.merge_select_pairs_rank_major(p, k)
+        for t in range(rows):
+            exp = brute.merge_pairs_row([[(int(p[r, t, j, 0]) & 0xFFFFFFFF, int(p[r, t, j, 1]))
+                                          for j in range(kc)] for r in range(world)], world, kc, k)
+            assert got[t].tolist() == exp, (trial, t)
+
+
+def test_pack_pairs_and_identity():
+    # W local top-K lists (N = K) contain the global top-K: the pair select over
+    # them equals the direct top-K of the global row.
+    world, s, k, rows = 4, 600, 64, 10
+    rng = np.random.default_rng(12)
+    g = rng.standard_normal((rows, world * s)).astype(np.float32)
+    ranks = datagen.rank_slices(g, world)
+    pairs = np.stack([oracle.pack_pairs(ranks[r], oracle.topk_rows(ranks[r], None, k), r, world)
+                      for r in range(world)])
+    ids = oracle.merge_select_pairs_rank_major(pairs, k)
+    for t in range(rows):
+        direct = np.argsort(-g[t], kind="stable")[:k]
+        assert set(ids[t].tolist()) == set(direct.tolist())
+    # pack_pairs fields: score bits and gid = local * W + r
+    loc = oracle.topk_rows(ranks[2], None, k)
+    pp = oracle.pack_pairs(ranks[2], loc, 2, world)
+    assert (pp[..., 1] == loc * world + 2).all()
+    assert (pp[..., 0].view(np.float32) == np.take_along_axis(ranks[2], loc, 1)).all()
+
+
+def test_pack_pairs_drops():
+    x = np.array([[1.0, np.nan, 3.0, 4.0]], np.float32)
+    idx = np.array([[0, 1, 2, 3, -1, 9]], np.int32)
+    pp = oracle.pack_pairs(x, idx, 1, 3, row_ends=np.array([3], np.int32))
+    assert pp[0, :, 1].tolist() == [1, -1, 7, -1, -1, -1]
+    assert pp[0, 0, 0].view(np.float32) == 1.0
+
+
+def test_producer_contract_on_oracle_pack():
+    # assert_packed_merge_contract's checks, restated, on oracle pack(topk) output.
+    rng = np.random.default_rng(2)
+    rows, cols, n = 16, 700, 96
+    x = datagen.bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32))
+    x[rng.random((rows, cols)) < 0.02] = 0x7FC0
+    ends = rng.integers(0, cols + 1, size=rows).astype(np.int32)
+    ends[0] = 50
+    packed = oracle.pack_candidates(x, oracle.topk_rows(x, ends, n), ends).view(np.uint32)
+    for t in range(rows):
+        words = packed[t, :n]
+        plane = packed[t, n:]
+        j = np.arange(n)
+        local = (0xFFFF - (words & 0xFFFF)) | (((plane[j // 32] >> (j % 32)) & 1) << 16)
+        sent = words != 0
+        e = int(ends[t])
+        valid = (x[t, :e] & 0x7FFF) <= 0x7F80
+        ids = local[sent].astype(np.int64)
+        assert ids.size == min(n, int(valid.sum()))
+        if ids.size == 0:
+            continue
+        assert ids.max() < e and len(np.unique(ids)) == ids.size
+        o = np.array([brute.ord16(int(b)) for b in x[t, :e]])
+        assert np.array_equal(words[sent] >> 16, o[ids])
+        unsent = valid.copy()
+        unsent[ids] = False
+        if unsent.any():
+            assert o[unsent].max() <= (words[sent] >> 16).min()
