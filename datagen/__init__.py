@@ -111,12 +111,18 @@ def logits(w: Workload, blocks=None, threads: int = 4) -> np.ndarray:
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round to nearest even; NaN stays NaN."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> 16) & 1
-    r = ((u.astype(np.uint64) + 0x7FFF + lsb) >> 16).astype(np.uint16)
-    nan = (u & 0x7FFFFFFF) > 0x7F800000
-    if nan.any():
-        r[nan] = ((u[nan] >> 16) | 0x0040).astype(np.uint16)
-    return r
+    out = np.empty(u.shape, np.uint16)
+    flat_u, flat_o = u.reshape(-1), out.reshape(-1)
+    step = 1 << 24
+    for i in range(0, flat_u.size, step):
+        c = flat_u[i:i + step]
+        # uint32 arithmetic: no non-NaN pattern can carry past bit 31
+        r = ((c + np.uint32(0x7FFF) + ((c >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
+        nan = (c & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+        if nan.any():
+            r[nan] = ((c[nan] >> 16) | np.uint32(0x0040)).astype(np.uint16)
+        flat_o[i:i + step] = r
+    return out
 
 
 def bf16_to_f32(b: np.ndarray) -> np.ndarray:

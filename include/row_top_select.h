@@ -1,0 +1,182 @@
+/*
+ * row_top_select -- batched per-row exact top-K selection over indexer logits,
+ * and the one-round candidate merge of a token-sharded (DCP) indexer, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources: the three pages this library follows.
+ *   [P1] vLLM pull request 65178 (rank-major DCP top-k merge): "Overview" and
+ *        "Details" -- (score, global id) candidates all-gathered along dim 0
+ *        into [W, R, K, 2] and selected in place.
+ *   [P2] vLLM API page vllm.models.kimi_k3.nvidia.ops.dcp_topk_merge.kernels:
+ *        module docstring (B' word and bit plane, exactness, saturation word),
+ *        DCPTopkPackKernel, DCPTopkSelectKernel, _decode_key, _ord16,
+ *        dcp_topk_pack_indices, dcp_topk_select, _check_exact.
+ *   [P3] vLLM pull request 57206, "Use DeepSelect for eligible sparse-indexer
+ *        prefill chunks": "Purpose" (causal per-row end, KV from column 0,
+ *        preallocated output) and "Test Plan" (short rows, -1 tails, strided
+ *        output, untouched padding, graph replay after updating row ends).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or retains memory and keeps no state.
+ *   - Every call only validates its arguments on the host and enqueues work on
+ *     `stream` (0 = the null stream); it never synchronises, so calls are
+ *     stream-ordered and may be captured into a HIP graph.  Data the kernels
+ *     read (row_ends included) is read on the device at execution time.
+ *   - Errors are reported by the return value (rts_status) before anything is
+ *     launched; a failed launch returns RTS_EHIP.  Data-dependent oddities
+ *     (NaN, out-of-range local ids, duplicate candidates) are defined
+ *     behaviour and never cause an out-of-bounds access.
+ *   - Scores order as IEEE values, descending, with -0.0 below +0.0 (the
+ *     order of the order-preserving key of [P2] _ord16); NaN is never a
+ *     candidate; +inf and -inf are ordinary candidates.  Equal scores are
+ *     resolved toward the lower id.
+ */
+#ifndef ROW_TOP_SELECT_H
+#define ROW_TOP_SELECT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RTS_OK = 0,
+    RTS_EINVAL = -1,       /* a null pointer, a negative size, a stride below its row, ... */
+    RTS_EUNSUPPORTED = -2, /* valid request outside what this build implements (e.g. k > 2048) */
+    RTS_EWORKSPACE = -3,   /* a workspace was given but is smaller than required */
+    RTS_EHIP = -4          /* the HIP runtime rejected the launch */
+} rts_status;
+
+typedef enum {
+    RTS_F32 = 0,  /* IEEE binary32 */
+    RTS_BF16 = 1  /* bfloat16 bit patterns (uint16_t) */
+} rts_dtype;
+
+/* Human-readable name of an rts_status value (static storage). */
+const char* rts_status_string(int status);
+
+/*
+ * Bytes of device workspace that lets topk_rows split long rows of a small
+ * batch over several workgroups (0 when no split is used for this shape).
+ * Passing less than this (but not 0) to topk_rows is RTS_EWORKSPACE; passing
+ * no workspace at all is allowed and runs every row in one workgroup.
+ */
+size_t topk_rows_workspace_size(int dtype, int64_t rows, int64_t cols, int32_t k);
+
+/*
+ * topk_rows -- exact top-k of every row ([P3] Purpose and Test Plan; selection
+ * rule of [P2] module docstring and DCPTopkSelectKernel docstring).
+ *
+ * logits    [rows, ld_logits] row-major, dtype RTS_F32 (float) or RTS_BF16
+ *           (uint16_t bits); only columns [0, cols) are ever read, and of row i
+ *           only columns [0, e_i).  Must be aligned to its element size.
+ * row_ends  int32 [rows] or NULL.  e_i = clamp(row_ends[i], 0, cols): the
+ *           exclusive causal end of row i, the row starting at column 0.
+ *           NULL means e_i = cols for every row.
+ * k         1 <= k <= 2048.
+ * out_idx   int32 [rows, ld_out], ld_out >= k.  Row i receives the column ids
+ *           of its m_i = min(k, #non-NaN in [0, e_i)) best entries in
+ *           (score desc, id asc) order, then -1 in columns [m_i, k).  Columns
+ *           [k, ld_out) are never written.
+ * workspace optional device scratch (see topk_rows_workspace_size), may be
+ *           NULL with workspace_bytes == 0.
+ * Errors: RTS_EINVAL (bad sizes/strides/pointers/dtype/alignment),
+ *         RTS_EUNSUPPORTED (k > 2048, cols >= 2^31), RTS_EWORKSPACE, RTS_EHIP.
+ */
+int topk_rows(const void* logits, int dtype, int64_t rows, int64_t cols, int64_t ld_logits,
+              const int32_t* row_ends, int32_t k, int32_t* out_idx, int64_t ld_out,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pack_candidates -- a rank's local top-n as B' words ([P2] module docstring
+ * step 1, DCPTopkPackKernel, dcp_topk_pack_indices).
+ *
+ * logits_bf16 [rows, ld_logits] bf16 bits; cols columns.
+ * local_idx   int32 [rows, ld_idx], ld_idx >= n: local column ids, -1 padded,
+ *             any order.
+ * n           number of slots, a positive multiple of 32.
+ * row_ends    int32 [rows] or NULL (= cols).
+ * packed      int32 [rows, n + n/32], contiguous.  For slot j with
+ *             l = local_idx[t, j] and end = min(row_end_t, cols, 2^17):
+ *               0 <= l < end and score not NaN:
+ *                 packed[t, j] = (ord16(score) << 16) | (0xFFFF - (l & 0xFFFF)),
+ *                 bit j%32 of packed[t, n + j/32] = bit 16 of l;
+ *               otherwise packed[t, j] = 0 (empty) and the plane bit is 0.
+ *             ord16(b) = b & 0x8000 ? ~b & 0xFFFF : b | 0x8000.
+ * Errors: RTS_EINVAL, RTS_EHIP.
+ */
+int pack_candidates(const uint16_t* logits_bf16, int64_t rows, int64_t cols, int64_t ld_logits,
+                    const int32_t* local_idx, int32_t n, int64_t ld_idx, const int32_t* row_ends,
+                    int32_t* packed, hipStream_t stream);
+
+/*
+ * merge_select_rank_major -- round-1 select of the packed merge ([P2] module
+ * docstring steps 2-3 and saturation, DCPTopkSelectKernel, _decode_key; the
+ * gathered buffer is read in place, rank-major, as in [P1]).
+ *
+ * gathered  int32 [world, rows, n + n/32], contiguous: rank r's packed rows.
+ *           A nonzero word w at (r, t, j) is the candidate
+ *             local = (0xFFFF - (w & 0xFFFF)) | (bit j%32 of gathered[r, t, n + j/32]) << 16,
+ *             gid = local * world + r, score key ord16 = w >> 16.
+ * world     1..16 ranks; n a positive multiple of 32; world * n <= 32768.
+ * k         1 <= k <= 2048.
+ * out_ids   int32 [rows, k], contiguous: the gids of the first min(k, count)
+ *           candidates under (ord16 desc, gid asc), listed in candidate order
+ *           (rank, then slot), then -1.
+ * sat_word  int32 [rows] or NULL: (mask << 16) | tau16, tau16 = ord16 of the
+ *           k-th selected (0 when fewer than k candidates), mask bit r set iff
+ *           all n words of rank r are nonzero with ord16 > tau16; a mask with
+ *           more than (k - 1) / n bits is cleared.  mask == 0 means round 1 is
+ *           exact.
+ * Candidates are expected to have distinct gids; with repeated words the
+ * output stays in bounds and deterministic but is not specified further.
+ * Errors: RTS_EINVAL, RTS_EUNSUPPORTED, RTS_EHIP.
+ */
+int merge_select_rank_major(const int32_t* gathered, int32_t world, int64_t rows, int32_t n,
+                            int32_t k, int32_t* out_ids, int32_t* sat_word, hipStream_t stream);
+
+/*
+ * pack_pairs -- a rank's local top-kc as (score, global id) pairs ([P1]
+ * Overview: "pack(local_topk)" into [R, K, 2]).
+ *
+ * logits    float [rows, ld_logits]; cols columns.
+ * local_idx int32 [rows, ld_idx], ld_idx >= kc: local column ids, -1 padded.
+ * row_ends  int32 [rows] or NULL (= cols).
+ * rank, world  0 <= rank < world; cols * world < 2^31.
+ * pairs     int32 [rows, kc, 2], contiguous: for l = local_idx[t, j] with
+ *           0 <= l < clamp(row_end_t, 0, cols) and x[t, l] not NaN:
+ *           (bits of x[t, l], l * world + rank); otherwise (0, -1).
+ * Errors: RTS_EINVAL, RTS_EHIP.
+ */
+int pack_pairs(const float* logits, int64_t rows, int64_t cols, int64_t ld_logits,
+               const int32_t* local_idx, int32_t kc, int64_t ld_idx, const int32_t* row_ends,
+               int32_t rank, int32_t world, int32_t* pairs, hipStream_t stream);
+
+/*
+ * merge_select_pairs_rank_major -- select from (score, global id) pairs read
+ * in place from the rank-major all-gather buffer ([P1] Overview and Details).
+ *
+ * gathered_pairs int32 [world, rows, kc, 2], contiguous: [..., 0] fp32 score
+ *           bits, [..., 1] global id; a negative id is an empty slot, a NaN
+ *           score is dropped.
+ * world >= 1, kc >= 1, world * kc <= 32768.  k: 1 <= k <= 2048.
+ * out_ids   int32 [rows, k], contiguous: the ids of the first min(k, count)
+ *           candidates under (score desc, -0 below +0, id asc), listed in
+ *           candidate order (rank, then slot), then -1.
+ * Ids are expected to be distinct within a row (as all-gathered local top-k
+ * lists are); repeated ids stay in bounds but are not specified further.
+ * Errors: RTS_EINVAL, RTS_EUNSUPPORTED, RTS_EHIP.
+ */
+int merge_select_pairs_rank_major(const int32_t* gathered_pairs, int32_t world, int64_t rows,
+                                  int32_t kc, int32_t k, int32_t* out_ids, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROW_TOP_SELECT_H */

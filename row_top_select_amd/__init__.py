@@ -1,0 +1,221 @@
+"""Python binding of the row_top_select C ABI (include/row_top_select.h).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``librow_top_select.so``.  PyTorch provides device memory and the current
+stream; tensors must live on the GPU.  Importing this package fails loudly if
+the library has not been built (``python -m row_top_select_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librow_top_select.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m row_top_select_amd.build` "
+        "(hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+RTS_OK, RTS_EINVAL, RTS_EUNSUPPORTED, RTS_EWORKSPACE, RTS_EHIP = 0, -1, -2, -3, -4
+RTS_F32, RTS_BF16 = 0, 1
+
+_i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+_lib.rts_status_string.argtypes = [ctypes.c_int]
+_lib.rts_status_string.restype = ctypes.c_char_p
+_lib.topk_rows_workspace_size.argtypes = [ctypes.c_int, _i64, _i64, _i32]
+_lib.topk_rows_workspace_size.restype = _sz
+_lib.topk_rows.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i32, _p, _i64, _p, _sz, _p]
+_lib.pack_candidates.argtypes = [_p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p, _p]
+_lib.merge_select_rank_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p, _p]
+_lib.pack_pairs.argtypes = [_p, _i64, _i64, _i64, _p, _i32, _i64, _p, _i32, _i32, _p, _p]
+_lib.merge_select_pairs_rank_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p]
+for _f in (_lib.topk_rows, _lib.pack_candidates, _lib.merge_select_rank_major, _lib.pack_pairs,
+           _lib.merge_select_pairs_rank_major):
+    _f.restype = ctypes.c_int
+
+
+class RtsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {rts_status_string(status)}")
+
+
+def rts_status_string(status: int) -> str:
+    return _lib.rts_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != RTS_OK:
+        raise RtsError(status, where)
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt(t, name):
+    return None if t is None else _dev(t, name)
+
+
+def _rows_ld(t: torch.Tensor, name: str):
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.shape[0], t.shape[1], (t.stride(0) if t.shape[0] > 1 else t.shape[1])
+
+
+def _int32_vec(t, rows, name):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] < rows or (rows > 1 and t.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous int32 vector of >= {rows} entries")
+    return t
+
+
+def topk_rows_workspace_size(dtype, rows: int, cols: int, k: int) -> int:
+    dt = RTS_BF16 if dtype in (torch.bfloat16, RTS_BF16) else RTS_F32
+    return int(_lib.topk_rows_workspace_size(dt, rows, cols, k))
+
+
+def topk_rows(logits: torch.Tensor, k: int, row_ends: torch.Tensor | None = None,
+              out: torch.Tensor | None = None, workspace="auto", stream=None) -> torch.Tensor:
+    """Exact per-row top-k column ids (score desc, id asc), -1 padded; see topk_rows in the header.
+
+    ``out`` may be wider than k (columns past k are left untouched).  ``workspace``:
+    "auto" (allocated here when the shape splits rows), None, or a uint8 GPU tensor.
+    """
+    if logits.dtype == torch.float32:
+        dt = RTS_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = RTS_BF16
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    rows, cols, ld = _rows_ld(logits, "logits")
+    row_ends = _int32_vec(row_ends, rows, "row_ends")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
+    if out.dtype != torch.int32:
+        raise TypeError("out must be int32")
+    _, _, ld_out = _rows_ld(out, "out")
+    if rows <= 1:
+        ld_out = max(ld_out, k)
+    ws, ws_bytes = None, 0
+    if isinstance(workspace, str) and workspace == "auto":
+        need = topk_rows_workspace_size(dt, rows, cols, k)
+        if need:
+            ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+            ws_bytes = need
+    elif workspace is not None:
+        ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
+    _check(_lib.topk_rows(_dev(logits, "logits"), dt, rows, cols, ld, _opt(row_ends, "row_ends"), k,
+                          _dev(out, "out"), ld_out, _opt(ws, "workspace"), ws_bytes, _stream(stream)),
+           "topk_rows")
+    return out
+
+
+def pack_candidates(logits_bf16: torch.Tensor, local_idx: torch.Tensor,
+                    row_ends: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """B' packed rows int32 [rows, n + n/32] of a local top-n; see pack_candidates in the header."""
+    if logits_bf16.dtype != torch.bfloat16:
+        raise TypeError("logits must be bfloat16")
+    rows, cols, ld = _rows_ld(logits_bf16, "logits")
+    if local_idx.dtype != torch.int32:
+        raise TypeError("local_idx must be int32")
+    r2, n, ld_idx = _rows_ld(local_idx, "local_idx")
+    if r2 != rows:
+        raise ValueError("local_idx must have one row per logits row")
+    if rows <= 1:
+        ld_idx = max(ld_idx, n)
+    row_ends = _int32_vec(row_ends, rows, "row_ends")
+    width = n + n // 32
+    if out is None:
+        out = torch.empty((rows, width), dtype=torch.int32, device=logits_bf16.device)
+    if out.dtype != torch.int32 or tuple(out.shape) != (rows, width) or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous int32 [{rows}, {width}]")
+    _check(_lib.pack_candidates(_dev(logits_bf16, "logits"), rows, cols, ld,
+                                _dev(local_idx, "local_idx"), n, ld_idx, _opt(row_ends, "row_ends"),
+                                _dev(out, "out"), _stream(stream)), "pack_candidates")
+    return out
+
+
+def merge_select_rank_major(gathered: torch.Tensor, k: int, out: torch.Tensor | None = None,
+                            sat_word: torch.Tensor | None = None, want_sat: bool = True,
+                            stream=None):
+    """Select from int32 [W, R, n + n/32]; returns (ids [R, k], sat_word [R] or None)."""
+    if gathered.dtype != torch.int32 or gathered.dim() != 3 or not gathered.is_contiguous():
+        raise ValueError("gathered must be contiguous int32 [W, R, n + n/32]")
+    world, rows, width = gathered.shape
+    n = width * 32 // 33
+    if n + n // 32 != width:
+        raise ValueError("gathered's last dimension must be n + n/32")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=gathered.device)
+    if out.dtype != torch.int32 or tuple(out.shape) != (rows, k) or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous int32 [{rows}, {k}]")
+    if sat_word is None and want_sat:
+        sat_word = torch.empty((rows,), dtype=torch.int32, device=gathered.device)
+    _check(_lib.merge_select_rank_major(_dev(gathered, "gathered"), world, rows, n, k, _dev(out, "out"),
+                                        _opt(sat_word, "sat_word"), _stream(stream)),
+           "merge_select_rank_major")
+    return out, sat_word
+
+
+def pack_pairs(logits: torch.Tensor, local_idx: torch.Tensor, rank: int, world: int,
+               row_ends: torch.Tensor | None = None, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """(score bits, gid) pairs int32 [rows, kc, 2]; see pack_pairs in the header."""
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be float32")
+    rows, cols, ld = _rows_ld(logits, "logits")
+    if local_idx.dtype != torch.int32:
+        raise TypeError("local_idx must be int32")
+    r2, kc, ld_idx = _rows_ld(local_idx, "local_idx")
+    if r2 != rows:
+        raise ValueError("local_idx must have one row per logits row")
+    if rows <= 1:
+        ld_idx = max(ld_idx, kc)
+    row_ends = _int32_vec(row_ends, rows, "row_ends")
+    if out is None:
+        out = torch.empty((rows, kc, 2), dtype=torch.int32, device=logits.device)
+    if out.dtype != torch.int32 or tuple(out.shape) != (rows, kc, 2) or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous int32 [{rows}, {kc}, 2]")
+    _check(_lib.pack_pairs(_dev(logits, "logits"), rows, cols, ld, _dev(local_idx, "local_idx"), kc,
+                           ld_idx, _opt(row_ends, "row_ends"), rank, world, _dev(out, "out"),
+                           _stream(stream)), "pack_pairs")
+    return out
+
+
+def merge_select_pairs_rank_major(gathered_pairs: torch.Tensor, k: int,
+                                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Select from int32 [W, R, kc, 2] read in place; returns ids [R, k]."""
+    g = gathered_pairs
+    if g.dtype != torch.int32 or g.dim() != 4 or g.shape[3] != 2 or not g.is_contiguous():
+        raise ValueError("gathered_pairs must be contiguous int32 [W, R, kc, 2]")
+    world, rows, kc, _ = g.shape
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=g.device)
+    if out.dtype != torch.int32 or tuple(out.shape) != (rows, k) or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous int32 [{rows}, {k}]")
+    _check(_lib.merge_select_pairs_rank_major(_dev(g, "gathered_pairs"), world, rows, kc, k,
+                                              _dev(out, "out"), _stream(stream)),
+           "merge_select_pairs_rank_major")
+    return out
+
+
+def raw_library() -> ctypes.CDLL:
+    """The loaded shared library (for ABI-level tests)."""
+    return _lib

@@ -1,0 +1,115 @@
+// The C ABI of row_top_select: argument validation on the host (nothing is
+// launched on a bad call, in the spirit of the host checks of _check_exact on
+// the kernels page of vllm.models.kimi_k3.nvidia.ops.dcp_topk_merge), then the
+// launchers next to the kernels.  No allocation, no synchronisation.
+#include "../../include/row_top_select.h"
+
+#include <stdint.h>
+
+#include "rts_internal.h"
+
+namespace {
+
+constexpr int32_t kMaxK = 2048;
+constexpr int64_t kMaxGrid = 0x7FFFFFFFll;
+constexpr int64_t kMaxCandidates = 32768;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* rts_status_string(int status) {
+    switch (status) {
+        case RTS_OK: return "RTS_OK";
+        case RTS_EINVAL: return "RTS_EINVAL: invalid argument";
+        case RTS_EUNSUPPORTED: return "RTS_EUNSUPPORTED: request outside this build's limits";
+        case RTS_EWORKSPACE: return "RTS_EWORKSPACE: workspace smaller than required";
+        case RTS_EHIP: return "RTS_EHIP: HIP launch failed";
+        default: return "unknown rts_status";
+    }
+}
+
+size_t topk_rows_workspace_size(int dtype, int64_t rows, int64_t cols, int32_t k) {
+    if ((dtype != RTS_F32 && dtype != RTS_BF16) || rows < 0 || cols < 0 || k < 1 || k > kMaxK)
+        return 0;
+    return rts::plan_topk_rows(dtype, rows, cols, k, true).ws_bytes;
+}
+
+int topk_rows(const void* logits, int dtype, int64_t rows, int64_t cols, int64_t ld_logits,
+              const int32_t* row_ends, int32_t k, int32_t* out_idx, int64_t ld_out, void* workspace,
+              size_t workspace_bytes, hipStream_t stream) {
+    if (dtype != RTS_F32 && dtype != RTS_BF16) return RTS_EINVAL;
+    if (rows < 0 || cols < 0 || ld_logits < cols || ld_logits < 0 || k < 1 || ld_out < k)
+        return RTS_EINVAL;
+    if (k > kMaxK || cols > 0x7FFFFFFFll) return RTS_EUNSUPPORTED;
+    if (rows == 0) return RTS_OK;
+    if (!out_idx || (cols > 0 && !logits)) return RTS_EINVAL;
+    const size_t esz = dtype == RTS_F32 ? 4 : 2;
+    if (!aligned(logits, esz) || !aligned(out_idx, 4) || (row_ends && !aligned(row_ends, 4)))
+        return RTS_EINVAL;
+    if (workspace_bytes > 0 && !workspace) return RTS_EINVAL;
+    const bool have_ws = workspace != nullptr;
+    rts::TopkPlan plan = rts::plan_topk_rows(dtype, rows, cols, k, have_ws);
+    if (have_ws && workspace_bytes < plan.ws_bytes) return RTS_EWORKSPACE;
+    if (have_ws && !aligned(workspace, 8)) return RTS_EINVAL;
+    if (rows * plan.groups > kMaxGrid) return RTS_EUNSUPPORTED;
+    return rts::launch_topk_rows(logits, dtype, rows, cols, ld_logits, row_ends, k, out_idx, ld_out,
+                                 plan, workspace, stream);
+}
+
+int pack_candidates(const uint16_t* logits_bf16, int64_t rows, int64_t cols, int64_t ld_logits,
+                    const int32_t* local_idx, int32_t n, int64_t ld_idx, const int32_t* row_ends,
+                    int32_t* packed, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || ld_logits < cols || n < 32 || n % 32 != 0 || ld_idx < n)
+        return RTS_EINVAL;
+    if (rows == 0) return RTS_OK;
+    if (!logits_bf16 || !local_idx || !packed) return RTS_EINVAL;
+    if (!aligned(logits_bf16, 2) || !aligned(local_idx, 4) || !aligned(packed, 4) ||
+        (row_ends && !aligned(row_ends, 4)))
+        return RTS_EINVAL;
+    if ((rows * (int64_t)n + 255) / 256 > kMaxGrid) return RTS_EUNSUPPORTED;
+    return rts::launch_pack_candidates(logits_bf16, rows, cols, ld_logits, local_idx, n, ld_idx,
+                                       row_ends, packed, stream);
+}
+
+int merge_select_rank_major(const int32_t* gathered, int32_t world, int64_t rows, int32_t n,
+                            int32_t k, int32_t* out_ids, int32_t* sat_word, hipStream_t stream) {
+    if (world < 1 || world > 16 || rows < 0 || n < 32 || n % 32 != 0 || k < 1) return RTS_EINVAL;
+    if (k > kMaxK || (int64_t)world * n > kMaxCandidates || rows > kMaxGrid) return RTS_EUNSUPPORTED;
+    if (rows == 0) return RTS_OK;
+    if (!gathered || !out_ids) return RTS_EINVAL;
+    if (!aligned(gathered, 4) || !aligned(out_ids, 4) || (sat_word && !aligned(sat_word, 4)))
+        return RTS_EINVAL;
+    return rts::launch_merge_packed(gathered, world, rows, n, k, out_ids, sat_word, stream);
+}
+
+int pack_pairs(const float* logits, int64_t rows, int64_t cols, int64_t ld_logits,
+               const int32_t* local_idx, int32_t kc, int64_t ld_idx, const int32_t* row_ends,
+               int32_t rank, int32_t world, int32_t* pairs, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || ld_logits < cols || kc < 1 || ld_idx < kc || world < 1 ||
+        rank < 0 || rank >= world)
+        return RTS_EINVAL;
+    if (cols * (int64_t)world > 0x7FFFFFFFll) return RTS_EUNSUPPORTED;
+    if (rows == 0) return RTS_OK;
+    if (!logits || !local_idx || !pairs) return RTS_EINVAL;
+    if (!aligned(logits, 4) || !aligned(local_idx, 4) || !aligned(pairs, 8) ||
+        (row_ends && !aligned(row_ends, 4)))
+        return RTS_EINVAL;
+    if ((rows * (int64_t)kc + 255) / 256 > kMaxGrid) return RTS_EUNSUPPORTED;
+    return rts::launch_pack_pairs(logits, rows, cols, ld_logits, local_idx, kc, ld_idx, row_ends,
+                                  rank, world, pairs, stream);
+}
+
+int merge_select_pairs_rank_major(const int32_t* gathered_pairs, int32_t world, int64_t rows,
+                                  int32_t kc, int32_t k, int32_t* out_ids, hipStream_t stream) {
+    if (world < 1 || rows < 0 || kc < 1 || k < 1) return RTS_EINVAL;
+    if (k > kMaxK || (int64_t)world * kc > kMaxCandidates || rows > kMaxGrid) return RTS_EUNSUPPORTED;
+    if (rows == 0) return RTS_OK;
+    if (!gathered_pairs || !out_ids) return RTS_EINVAL;
+    if (!aligned(gathered_pairs, 8) || !aligned(out_ids, 4)) return RTS_EINVAL;
+    return rts::launch_merge_pairs(gathered_pairs, world, rows, kc, k, out_ids, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Host-side launchers implemented next to their kernels and called by the
+// C ABI in rts_api.cpp after argument validation.  Each returns an rts_status.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rts {
+
+// Launch geometry of topk_rows for one problem shape.
+struct TopkPlan {
+    int e;          // sorted-list length per lane (list = 64 * e >= k)
+    int waves;      // waves per workgroup sharing one row
+    int groups;     // workgroups per row (> 1 needs a workspace)
+    size_t ws_bytes;
+};
+
+TopkPlan plan_topk_rows(int dtype, int64_t rows, int64_t cols, int32_t k, bool allow_split);
+
+int launch_topk_rows(const void* logits, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                     const int32_t* row_ends, int32_t k, int32_t* out, int64_t ld_out,
+                     const TopkPlan& plan, void* workspace, hipStream_t stream);
+
+int launch_pack_candidates(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                           const int32_t* local_idx, int32_t n, int64_t ld_idx,
+                           const int32_t* row_ends, int32_t* packed, hipStream_t stream);
+
+int launch_pack_pairs(const float* x, int64_t rows, int64_t cols, int64_t ld,
+                      const int32_t* local_idx, int32_t kc, int64_t ld_idx,
+                      const int32_t* row_ends, int32_t rank, int32_t world, int32_t* pairs,
+                      hipStream_t stream);
+
+int launch_merge_packed(const int32_t* gathered, int32_t world, int64_t rows, int32_t n,
+                        int32_t k, int32_t* out_ids, int32_t* sat_word, hipStream_t stream);
+
+int launch_merge_pairs(const int32_t* pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
+                       int32_t* out_ids, hipStream_t stream);
+
+}  // namespace rts

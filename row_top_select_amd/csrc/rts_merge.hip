@@ -1,0 +1,490 @@
+// Candidate packing and the rank-major merge selects, for gfx950.
+//
+// Sources (the kernels page of vllm.models.kimi_k3.nvidia.ops.dcp_topk_merge
+// and vLLM PR 65178 "rank-major DCP top-k merge"):
+//   * pack: B' word (ord16(score) << 16) | (0xFFFF - local[15:0]) plus a bit
+//     plane holding local[16], one plane word per 32 slots; ids outside
+//     [0, min(row_end, S, 2^17)) and NaN scores pack as 0 (module docstring
+//     step 1, DCPTopkPackKernel, dcp_topk_pack_indices).
+//   * packed select: decode every nonzero word to gid = local * W + r and the
+//     score key ord16, keep the top k under (ord16 desc, gid asc), and derive
+//     sat_word = (mask << 16) | tau16 (module docstring, DCPTopkSelectKernel,
+//     _decode_key).
+//   * pair select: (score, gid) candidates of the all-gathered [W, R, K, 2]
+//     buffer read in place (PR 65178 Overview and Details).
+// Both selects run one 512-thread workgroup per row with every candidate in
+// registers as a 64-bit composite (key << 32) | (0xFFFFFFFF - gid).  The k-th
+// composite is found by a radix select whose 256 bins at each level span
+// [min, max] of the composites still in play (so a narrow score range still
+// spreads over the bins); histogram atomics go to 16 lane-striped LDS copies
+// at a 257-word stride, so lanes that share a digit mostly hit different
+// addresses and banks.  Selected ids are written in candidate order (rank,
+// then slot), a fixed order that does not depend on the launch geometry.
+#include "rts_device.hpp"
+#include "rts_internal.h"
+#include "../../include/row_top_select.h"
+
+namespace rts {
+
+constexpr int kSelBlock = 512;
+constexpr int kSelWaves = kSelBlock / kWave;
+constexpr int kHistCopies = 16;
+constexpr int kHistStride = 257;
+constexpr int kMaxTab = 64 * kSelWaves;  // KPT * waves entries of the emission table
+
+struct SelectSmem {
+    uint32_t hist[kHistCopies][kHistStride];
+    uint32_t bins[256];
+    uint64_t red_lo[kSelWaves];
+    uint64_t red_hi[kSelWaves];
+    uint32_t red_n[kSelWaves];
+    uint32_t scal[4];
+    uint32_t tab[kMaxTab];
+    uint32_t wsum[kSelWaves];
+    uint32_t notsat;
+};
+
+// ---------------------------------------------------------------------------
+// Block-level pieces (all threads of the workgroup call them)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, SelectSmem& sm) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    v = wave_sum32(v);
+    if (lane == 0) sm.red_n[wave] = v;
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) t += sm.red_n[w];
+    __syncthreads();
+    return t;
+}
+
+// Exclusive scan of one value per thread (thread order); returns the total.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& excl, SelectSmem& sm) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const uint32_t incl = wave_incl_scan32(v);
+    if (lane == kWave - 1) sm.wsum[wave] = incl;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        const uint32_t s = sm.wsum[w];
+        off += w < wave ? s : 0u;
+        tot += s;
+    }
+    __syncthreads();
+    excl = off + incl - v;
+    return tot;
+}
+
+// The smallest composite T such that exactly k nonzero keys are >= T (keys
+// distinct); requires k <= number of nonzero keys.  With repeated keys more
+// than k may be >= T.
+template <int KPT>
+__device__ uint64_t block_radix_kth(const uint64_t (&key)[KPT], int k, SelectSmem& sm) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    uint64_t lo_edge = 1, hi_edge = ~0ull;
+    int need = k;
+    // Each level narrows the range by at least 2^7; the cap only bounds the
+    // loop if the count invariant were ever broken.
+    for (int level = 0;; ++level) {
+        uint64_t mn = ~0ull, mx = 0;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const bool in = key[i] >= lo_edge && key[i] <= hi_edge;
+            mn = in ? umin64(mn, key[i]) : mn;
+            mx = in ? umax64(mx, key[i]) : mx;
+        }
+        mn = wave_min64(mn);
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) mx = umax64(mx, shfl_xor64(mx, d));
+        if (lane == 0) {
+            sm.red_lo[wave] = mn;
+            sm.red_hi[wave] = mx;
+        }
+        __syncthreads();
+        mn = ~0ull;
+        mx = 0;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w) {
+            mn = umin64(mn, sm.red_lo[w]);
+            mx = umax64(mx, sm.red_hi[w]);
+        }
+        if (mn == mx) return mn;
+        const uint64_t d = mx - mn;
+        const int bl = 64 - __clzll((long long)d);
+        const int s = bl > 8 ? bl - 8 : 0;
+        uint32_t* hcopy = sm.hist[lane & (kHistCopies - 1)];
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            if (key[i] >= lo_edge && key[i] <= hi_edge)
+                __hip_atomic_fetch_add(&hcopy[(uint32_t)((key[i] - mn) >> s)], 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        __syncthreads();
+        if (threadIdx.x < 256) {
+            uint32_t t = 0;
+#pragma unroll
+            for (int c = 0; c < kHistCopies; ++c) {
+                t += sm.hist[c][threadIdx.x];
+                sm.hist[c][threadIdx.x] = 0u;
+            }
+            sm.bins[threadIdx.x] = t;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            uint32_t c[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[j] = sm.bins[255 - 4 * lane - j];
+            const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+            uint32_t run = wave_incl_scan32(tot) - tot;
+            bool found = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (run < (uint32_t)need && run + c[j] >= (uint32_t)need) {
+                    sm.scal[0] = 255u - 4u * (uint32_t)lane - (uint32_t)j;
+                    sm.scal[1] = run;
+                    sm.scal[2] = c[j];
+                    found = true;
+                }
+                run += c[j];
+            }
+            // Defensive: with the count invariant broken, end at the range minimum.
+            if (__ballot(found) == 0ull && lane == 0) {
+                sm.scal[0] = 0u;
+                sm.scal[1] = 0u;
+                sm.scal[2] = (uint32_t)need;
+            }
+        }
+        __syncthreads();
+        const uint32_t bin = sm.scal[0];
+        const uint32_t above = sm.scal[1];
+        const uint32_t cb = sm.scal[2];
+        need -= (int)above;
+        const uint64_t blo = mn + ((uint64_t)bin << s);
+        if ((int)cb == need || level >= 12) return blo;
+        lo_edge = blo;
+        hi_edge = bin == (uint32_t)(d >> s) ? mx : blo + ((1ull << s) - 1ull);
+    }
+}
+
+// Selection of the keys >= T, written in flat candidate order
+// (f = i * kSelBlock + thread) into out[0, k), then -1 up to k.
+template <int KPT>
+__device__ void block_emit(const uint64_t (&key)[KPT], uint64_t T, int k, int32_t* __restrict__ out,
+                           SelectSmem& sm) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    uint64_t m[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        m[i] = __ballot(key[i] != 0ull && key[i] >= T);
+        if (lane == 0) sm.tab[i * kSelWaves + wave] = (uint32_t)__popcll(m[i]);
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    static_assert(KPT * kSelWaves <= kSelBlock, "one table entry per thread");
+    const uint32_t v = t < KPT * kSelWaves ? sm.tab[t] : 0u;
+    uint32_t excl;
+    const uint32_t total = block_excl_scan(v, excl, sm);
+    if (t < KPT * kSelWaves) sm.tab[t] = excl;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        if ((m[i] >> lane) & 1ull) {
+            const uint32_t pos = sm.tab[i * kSelWaves + wave] + mbcnt64(m[i]);
+            if (pos < (uint32_t)k) out[pos] = (int32_t)composite_id(key[i]);
+        }
+    }
+    const int filled = total < (uint32_t)k ? (int)total : k;
+    for (int p = filled + t; p < k; p += kSelBlock) out[p] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// Kernels
+// ---------------------------------------------------------------------------
+
+// One thread per slot; a half-wave covers 32 consecutive slots of one row
+// (n is a multiple of 32), so its ballot half is the plane word.
+__global__ __launch_bounds__(256) void pack_candidates_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    const int32_t* __restrict__ local_idx, int32_t n, int64_t ld_idx,
+    const int32_t* __restrict__ row_ends, int32_t* __restrict__ packed) {
+    const int64_t gidx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool in = gidx < rows * (int64_t)n;
+    const int64_t t = in ? gidx / n : 0;
+    const int32_t j = in ? (int32_t)(gidx - t * n) : 0;
+    const int64_t width = (int64_t)n + n / 32;
+    uint32_t word = 0;
+    bool high = false;
+    if (in) {
+        int64_t end = cols < (1 << 17) ? cols : (1 << 17);
+        if (row_ends && (int64_t)row_ends[t] < end) end = row_ends[t];
+        const int32_t l = local_idx[t * ld_idx + j];
+        if (l >= 0 && (int64_t)l < end) {
+            const uint32_t b = x[t * ld + l];
+            if ((b & 0x7FFFu) <= 0x7F80u) {
+                const uint32_t o = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+                word = (o << 16) | (0xFFFFu - ((uint32_t)l & 0xFFFFu));
+                high = (((uint32_t)l >> 16) & 1u) != 0u;
+            }
+        }
+        packed[t * width + j] = (int32_t)word;
+    }
+    const uint64_t m = __ballot(high);
+    const int lane = lane_id();
+    if (in && (lane & 31) == 0)
+        packed[t * width + n + j / 32] = (int32_t)(lane < 32 ? (uint32_t)m : (uint32_t)(m >> 32));
+}
+
+__global__ __launch_bounds__(256) void pack_pairs_kernel(
+    const float* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    const int32_t* __restrict__ local_idx, int32_t kc, int64_t ld_idx,
+    const int32_t* __restrict__ row_ends, int32_t rank, int32_t world, int32_t* __restrict__ pairs) {
+    const int64_t gidx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gidx >= rows * (int64_t)kc) return;
+    const int64_t t = gidx / kc;
+    const int32_t j = (int32_t)(gidx - t * kc);
+    int64_t end = row_ends ? (int64_t)row_ends[t] : cols;
+    end = end < 0 ? 0 : (end > cols ? cols : end);
+    const int32_t l = local_idx[t * ld_idx + j];
+    int32_t s = 0, id = -1;
+    if (l >= 0 && (int64_t)l < end) {
+        const uint32_t u = __float_as_uint(x[t * ld + l]);
+        if (!f32_bits_is_nan(u)) {
+            s = (int32_t)u;
+            id = l * world + rank;
+        }
+    }
+    typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+    i32x2 pr;
+    pr[0] = s;
+    pr[1] = id;
+    reinterpret_cast<i32x2*>(pairs)[gidx] = pr;
+}
+
+// flat candidate index f = i * kSelBlock + thread  ->  (rank r, slot j)
+struct FlatWalk {
+    int32_t r, j, q0, r0, n;
+    __device__ FlatWalk(int32_t n_, int32_t t) : n(n_) {
+        r = t / n_;
+        j = t - r * n_;
+        q0 = kSelBlock / n_;
+        r0 = kSelBlock - q0 * n_;
+    }
+    __device__ void next() {
+        r += q0;
+        j += r0;
+        if (j >= n) {
+            j -= n;
+            ++r;
+        }
+    }
+};
+
+template <int KPT>
+__global__ __launch_bounds__(kSelBlock) void merge_packed_kernel(
+    const int32_t* __restrict__ gathered, int32_t world, int64_t rows, int32_t n, int32_t k,
+    int32_t* __restrict__ out_ids, int32_t* __restrict__ sat_word) {
+    __shared__ SelectSmem sm;
+    const int t = threadIdx.x, lane = lane_id();
+    const int64_t row = blockIdx.x;
+    const int64_t width = (int64_t)n + n / 32;
+    const int32_t total = world * n;
+
+    for (int q = t; q < kHistCopies * kHistStride; q += kSelBlock) (&sm.hist[0][0])[q] = 0u;
+    if (t == 0) sm.notsat = 0u;
+
+    uint64_t key[KPT];
+    {
+        FlatWalk w(n, t);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            key[i] = 0ull;
+            if (i * kSelBlock + t < total) {
+                const int32_t* rowp = gathered + ((int64_t)w.r * rows + row) * width;
+                const uint32_t word = (uint32_t)rowp[w.j];
+                const uint32_t plane = (uint32_t)rowp[n + (w.j >> 5)];
+                if (word != 0u) {
+                    const uint32_t local =
+                        (0xFFFFu - (word & 0xFFFFu)) | (((plane >> (w.j & 31)) & 1u) << 16);
+                    const uint32_t gid = local * (uint32_t)world + (uint32_t)w.r;
+                    key[i] = composite(word >> 16, gid);
+                }
+            }
+            w.next();
+        }
+    }
+    uint32_t nz = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) nz += key[i] != 0ull;
+    __syncthreads();
+    const uint32_t nvalid = block_sum(nz, sm);
+
+    uint64_t T = 1ull;
+    if (nvalid > (uint32_t)k) T = block_radix_kth<KPT>(key, k, sm);
+    block_emit<KPT>(key, T, k, out_ids + row * (int64_t)k, sm);
+
+    if (sat_word) {
+        // tau16: ord16 of the k-th selected composite (the smallest selected).
+        uint64_t mn = ~0ull;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) mn = (key[i] != 0ull && key[i] >= T) ? umin64(mn, key[i]) : mn;
+        mn = wave_min64(mn);
+        const int wave = t / kWave;
+        if (lane == 0) sm.red_lo[wave] = mn;
+        __syncthreads();
+        mn = ~0ull;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w) mn = umin64(mn, sm.red_lo[w]);
+        const uint32_t tau = nvalid >= (uint32_t)k ? (uint32_t)(mn >> 32) : 0u;
+        // Rank r is saturated iff all its n words are nonzero with ord16 > tau.
+        FlatWalk w(n, t);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const bool cand = i * kSelBlock + t < total;
+            const bool bad = cand && (key[i] == 0ull || (uint32_t)(key[i] >> 32) <= tau);
+            const uint32_t bits = wave_or32(bad ? (1u << w.r) : 0u);
+            if (lane == 0 && bits)
+                __hip_atomic_fetch_or(&sm.notsat, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            w.next();
+        }
+        __syncthreads();
+        if (t == 0) {
+            uint32_t mask = ~sm.notsat & ((1u << world) - 1u);
+            if (__popc(mask) > (k - 1) / n) mask = 0u;
+            sat_word[row] = (int32_t)((mask << 16) | tau);
+        }
+    }
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kSelBlock) void merge_pairs_kernel(
+    const int32_t* __restrict__ pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
+    int32_t* __restrict__ out_ids) {
+    __shared__ SelectSmem sm;
+    typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int32_t total = world * kc;
+
+    for (int q = t; q < kHistCopies * kHistStride; q += kSelBlock) (&sm.hist[0][0])[q] = 0u;
+
+    uint64_t key[KPT];
+    {
+        FlatWalk w(kc, t);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            key[i] = 0ull;
+            if (i * kSelBlock + t < total) {
+                const i32x2 pr =
+                    reinterpret_cast<const i32x2*>(pairs)[((int64_t)w.r * rows + row) * kc + w.j];
+                const uint32_t u = (uint32_t)pr[0];
+                if (pr[1] >= 0 && !f32_bits_is_nan(u)) key[i] = composite(key32_of_bits(u), (uint32_t)pr[1]);
+            }
+            w.next();
+        }
+    }
+    uint32_t nz = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) nz += key[i] != 0ull;
+    __syncthreads();
+    const uint32_t nvalid = block_sum(nz, sm);
+
+    uint64_t T = 1ull;
+    if (nvalid > (uint32_t)k) T = block_radix_kth<KPT>(key, k, sm);
+    block_emit<KPT>(key, T, k, out_ids + row * (int64_t)k, sm);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace {
+
+int pick_kpt(int64_t total) {
+    const int64_t need = (total + kSelBlock - 1) / kSelBlock;
+    static const int choices[] = {1, 2, 4, 6, 8, 12, 16, 24, 32, 48, 64};
+    for (int c : choices)
+        if (c >= need) return c;
+    return -1;
+}
+
+template <template <int> class L, typename... A>
+int dispatch_kpt(int kpt, A... args) {
+    switch (kpt) {
+        case 1: L<1>::run(args...); break;
+        case 2: L<2>::run(args...); break;
+        case 4: L<4>::run(args...); break;
+        case 6: L<6>::run(args...); break;
+        case 8: L<8>::run(args...); break;
+        case 12: L<12>::run(args...); break;
+        case 16: L<16>::run(args...); break;
+        case 24: L<24>::run(args...); break;
+        case 32: L<32>::run(args...); break;
+        case 48: L<48>::run(args...); break;
+        case 64: L<64>::run(args...); break;
+        default: return RTS_EUNSUPPORTED;
+    }
+    return RTS_OK;
+}
+
+template <int KPT>
+struct PackedLaunch {
+    static void run(const int32_t* g, int32_t world, int64_t rows, int32_t n, int32_t k, int32_t* ids,
+                    int32_t* sat, hipStream_t s) {
+        hipLaunchKernelGGL((merge_packed_kernel<KPT>), dim3((unsigned)rows), dim3(kSelBlock), 0, s, g,
+                           world, rows, n, k, ids, sat);
+    }
+};
+
+template <int KPT>
+struct PairsLaunch {
+    static void run(const int32_t* p, int32_t world, int64_t rows, int32_t kc, int32_t k, int32_t* ids,
+                    hipStream_t s) {
+        hipLaunchKernelGGL((merge_pairs_kernel<KPT>), dim3((unsigned)rows), dim3(kSelBlock), 0, s, p,
+                           world, rows, kc, k, ids);
+    }
+};
+
+}  // namespace
+
+int launch_pack_candidates(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                           const int32_t* local_idx, int32_t n, int64_t ld_idx,
+                           const int32_t* row_ends, int32_t* packed, hipStream_t s) {
+    const int64_t total = rows * (int64_t)n;
+    if (total == 0) return RTS_OK;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(pack_candidates_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, cols, ld,
+                       local_idx, n, ld_idx, row_ends, packed);
+    return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
+}
+
+int launch_pack_pairs(const float* x, int64_t rows, int64_t cols, int64_t ld, const int32_t* local_idx,
+                      int32_t kc, int64_t ld_idx, const int32_t* row_ends, int32_t rank, int32_t world,
+                      int32_t* pairs, hipStream_t s) {
+    const int64_t total = rows * (int64_t)kc;
+    if (total == 0) return RTS_OK;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(pack_pairs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, cols, ld,
+                       local_idx, kc, ld_idx, row_ends, rank, world, pairs);
+    return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
+}
+
+int launch_merge_packed(const int32_t* gathered, int32_t world, int64_t rows, int32_t n, int32_t k,
+                        int32_t* out_ids, int32_t* sat_word, hipStream_t s) {
+    if (rows == 0) return RTS_OK;
+    const int kpt = pick_kpt((int64_t)world * n);
+    const int rc = dispatch_kpt<PackedLaunch>(kpt, gathered, world, rows, n, k, out_ids, sat_word, s);
+    if (rc != RTS_OK) return rc;
+    return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
+}
+
+int launch_merge_pairs(const int32_t* pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
+                       int32_t* out_ids, hipStream_t s) {
+    if (rows == 0) return RTS_OK;
+    const int kpt = pick_kpt((int64_t)world * kc);
+    const int rc = dispatch_kpt<PairsLaunch>(kpt, pairs, world, rows, kc, k, out_ids, s);
+    if (rc != RTS_OK) return rc;
+    return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
+}
+
+}  // namespace rts

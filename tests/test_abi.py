@@ -1,0 +1,103 @@
+"""The C-ABI library: it loads, exports every symbol the header declares, and
+rejects invalid arguments on the host before touching the GPU (no compute call
+happens in these tests, so they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "row_top_select.h")
+LIB = os.path.join(ROOT, "row_top_select_amd", "librow_top_select.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from row_top_select_amd import build as b
+        b.build(verbose=False)
+    lib = ctypes.CDLL(LIB)
+    i64, i32, p, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    lib.topk_rows.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, i64, p, sz, p]
+    lib.pack_candidates.argtypes = [p, i64, i64, i64, p, i32, i64, p, p, p]
+    lib.merge_select_rank_major.argtypes = [p, i32, i64, i32, i32, p, p, p]
+    lib.pack_pairs.argtypes = [p, i64, i64, i64, p, i32, i64, p, i32, i32, p, p]
+    lib.merge_select_pairs_rank_major.argtypes = [p, i32, i64, i32, i32, p, p]
+    lib.topk_rows_workspace_size.argtypes = [ctypes.c_int, i64, i64, i32]
+    lib.topk_rows_workspace_size.restype = sz
+    lib.rts_status_string.argtypes = [ctypes.c_int]
+    lib.rts_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"topk_rows", "pack_candidates", "merge_select_rank_major", "pack_pairs",
+                          "merge_select_pairs_rank_major", "topk_rows_workspace_size",
+                          "rts_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.rts_status_string(code).startswith(b"RTS_")
+    assert lib.rts_status_string(7) == b"unknown rts_status"
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+
+
+def test_topk_rows_validation(lib):
+    EINVAL, EUNSUP, EWS = -1, -2, -3
+    f = lib.topk_rows
+    assert f(FAKE, 2, 4, 8, 8, None, 2, FAKE, 2, None, 0, None) == EINVAL      # dtype
+    assert f(FAKE, 0, -1, 8, 8, None, 2, FAKE, 2, None, 0, None) == EINVAL     # rows < 0
+    assert f(FAKE, 0, 4, 8, 7, None, 2, FAKE, 2, None, 0, None) == EINVAL      # ld < cols
+    assert f(FAKE, 0, 4, 8, 8, None, 0, FAKE, 2, None, 0, None) == EINVAL      # k < 1
+    assert f(FAKE, 0, 4, 8, 8, None, 3, FAKE, 2, None, 0, None) == EINVAL      # ld_out < k
+    assert f(FAKE, 0, 4, 8, 8, None, 2049, FAKE, 4096, None, 0, None) == EUNSUP
+    assert f(None, 0, 4, 8, 8, None, 2, FAKE, 2, None, 0, None) == EINVAL      # null logits
+    assert f(FAKE, 0, 4, 8, 8, None, 2, None, 2, None, 0, None) == EINVAL      # null out
+    assert f(ctypes.c_void_p(0x10002), 0, 4, 8, 8, None, 2, FAKE, 2, None, 0, None) == EINVAL
+    assert f(FAKE, 0, 4, 8, 8, None, 2, FAKE, 2, None, 64, None) == EINVAL     # bytes, no ptr
+    # a split shape with a too-small workspace
+    need = lib.topk_rows_workspace_size(0, 64, 102400, 512)
+    assert need > 0
+    assert f(FAKE, 0, 64, 102400, 102400, None, 512, FAKE, 512, FAKE, need - 8, None) == EWS
+    assert f(FAKE, 0, 0, 8, 8, None, 2, FAKE, 2, None, 0, None) == 0           # nothing to do
+
+
+def test_workspace_size(lib):
+    assert lib.topk_rows_workspace_size(0, 4096, 102400, 512) == 0   # one wave per row suffices
+    assert lib.topk_rows_workspace_size(0, 64, 102400, 512) % (512 * 8) == 0
+    assert lib.topk_rows_workspace_size(5, 4, 4, 4) == 0
+
+
+def test_merge_and_pack_validation(lib):
+    EINVAL, EUNSUP = -1, -2
+    assert lib.pack_candidates(FAKE, 4, 8, 8, FAKE, 48, 48, None, FAKE, None) == EINVAL   # n % 32
+    assert lib.pack_candidates(FAKE, 4, 8, 8, FAKE, 32, 16, None, FAKE, None) == EINVAL   # ld_idx
+    assert lib.merge_select_rank_major(FAKE, 17, 4, 32, 64, FAKE, None, None) == EINVAL   # world
+    assert lib.merge_select_rank_major(FAKE, 0, 4, 32, 64, FAKE, None, None) == EINVAL
+    assert lib.merge_select_rank_major(FAKE, 8, 4, 40, 64, FAKE, None, None) == EINVAL    # n % 32
+    assert lib.merge_select_rank_major(FAKE, 8, 4, 32, 4096, FAKE, None, None) == EUNSUP  # k
+    assert lib.merge_select_rank_major(FAKE, 16, 4, 4096, 512, FAKE, None, None) == EUNSUP
+    assert lib.merge_select_rank_major(None, 8, 4, 32, 64, FAKE, None, None) == EINVAL
+    assert lib.pack_pairs(FAKE, 4, 8, 8, FAKE, 4, 4, None, 3, 3, FAKE, None) == EINVAL     # rank
+    assert lib.pack_pairs(FAKE, 4, 8, 8, FAKE, 4, 4, None, 0, 3, ctypes.c_void_p(0x10004),
+                          None) == EINVAL                                                  # align
+    assert lib.pack_pairs(FAKE, 4, 1 << 30, 1 << 30, FAKE, 4, 4, None, 0, 4, FAKE,
+                          None) == EUNSUP                                                  # gid range
+    assert lib.merge_select_pairs_rank_major(FAKE, 8, 4, 8192, 512, FAKE, None) == EUNSUP
+    assert lib.merge_select_pairs_rank_major(FAKE, 8, 4, 64, 0, FAKE, None) == EINVAL

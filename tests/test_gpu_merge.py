@@ -1,0 +1,197 @@
+"""GPU parity of pack_candidates, merge_select_rank_major, pack_pairs and
+merge_select_pairs_rank_major against the CPU oracle (bit-exact ids, words and
+saturation words), on random and constructed inputs and on the merge workload
+(8 simulated ranks, 6710 rows) at full size with sampled oracle rows.
+
+Inputs of the merge selects are built by the oracle (or by hand), never by the
+GPU path."""
+
+import numpy as np
+import pytest
+
+import brute
+import datagen
+import oracle
+from gpu_common import assert_ids_equal, bf16_dev, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def rts():
+    import row_top_select_amd
+    return row_top_select_amd
+
+
+def test_pack_random(rts):
+    rng = np.random.default_rng(11)
+    for n in (32, 64, 96, 384):
+        rows, cols = 37, int(rng.integers(100, 140000))
+        x = datagen.bf16_bits(rng.standard_normal((rows, cols)).astype(np.float32))
+        x[rng.random((rows, cols)) < 0.02] = 0x7FC0
+        idx = rng.integers(-3, cols + 5, size=(rows, n)).astype(np.int32)
+        ends = rng.integers(-1, cols + 10, size=rows).astype(np.int32)
+        for use_ends in (True, False):
+            say("pack", n, cols, use_ends)
+            e = ends if use_ends else None
+            got = host(rts.pack_candidates(bf16_dev(x), dev(idx), row_ends=None if e is None else dev(e)))
+            exp = oracle.pack_candidates(x, idx, e)
+            assert_ids_equal(got, exp, f"pack n={n}")
+
+
+def _gathered(rng, world, rows, n, fill=0.9, ties=False):
+    g = np.zeros((world, rows, n + n // 32), np.uint32)
+    for r in range(world):
+        for t in range(rows):
+            locs = rng.choice(1 << 17, size=n, replace=False)
+            if ties:
+                b = (rng.integers(0, 6, size=n) + 0x3F80).astype(np.uint16)
+            else:
+                b = datagen.bf16_bits(rng.standard_normal(n).astype(np.float32))
+            keep = rng.random(n) < fill
+            o = np.where(b & 0x8000, ~b.astype(np.uint32) & 0xFFFF, b.astype(np.uint32) | 0x8000)
+            w = (o << 16) | (0xFFFF - (locs & 0xFFFF))
+            g[r, t, :n] = np.where(keep, w, 0)
+            hi = ((locs >> 16) & 1) & keep
+            for j in np.nonzero(hi)[0]:
+                g[r, t, n + j // 32] |= np.uint32(1 << (j % 32))
+    return g.view(np.int32)
+
+
+@pytest.mark.parametrize("world,n,k,fill,ties", [
+    (8, 384, 2048, 1.0, False), (8, 384, 2048, 0.6, False), (8, 384, 2048, 1.0, True),
+    (4, 64, 100, 0.9, False), (1, 32, 32, 1.0, False), (16, 256, 1024, 0.95, True),
+    (3, 96, 2048, 0.8, False), (8, 2048, 512, 1.0, False)])
+def test_merge_packed_random(rts, world, n, k, fill, ties):
+    rng = np.random.default_rng(world * 1000 + n + k)
+    g = _gathered(rng, world, 40, n, fill, ties)
+    say("merge packed", world, n, k, fill, ties)
+    ids, sat = rts.merge_select_rank_major(dev(g), k)
+    eids, esat = oracle.merge_select_rank_major(g, k)
+    assert_ids_equal(host(ids), eids, "ids")
+    assert np.array_equal(host(sat), esat), "sat_word"
+
+
+def test_merge_packed_saturation_constructed(rts):
+    # rank 1 holds every top score: its bit is set, and the output matches the oracle
+    world, s, n, k, rows = 8, 2048, 96, 512, 16
+    rng = np.random.default_rng(4)
+    gl = rng.standard_normal((rows, world * s)).astype(np.float32)
+    gl[:, 1::world] += 10.0
+    gb = datagen.bf16_bits(gl)
+    ranks = datagen.rank_slices(gb, world)
+    packed = np.stack([oracle.pack_candidates(ranks[r], oracle.topk_rows(ranks[r], None, n))
+                       for r in range(world)])
+    say("saturation")
+    ids, sat = rts.merge_select_rank_major(dev(packed), k)
+    eids, esat = oracle.merge_select_rank_major(packed, k)
+    assert_ids_equal(host(ids), eids, "ids")
+    assert np.array_equal(host(sat), esat)
+    assert ((host(sat).view(np.uint32) >> 16) == 0b10).all()
+
+
+def test_merge_packed_duplicates_stay_in_bounds(rts):
+    # repeated words are outside the contract: only in-range, deterministic output is required
+    rng = np.random.default_rng(6)
+    world, n, k, rows = 4, 64, 128, 8
+    g = _gathered(rng, world, rows, n, 1.0, True)
+    g[1] = g[0]
+    say("duplicates")
+    out = torch.full((rows, k), 12345, dtype=torch.int32, device="cuda")
+    ids, sat = rts.merge_select_rank_major(dev(g), k, out=out)
+    a = host(ids)
+    ids2, _ = rts.merge_select_rank_major(dev(g), k)
+    assert np.array_equal(a, host(ids2))
+    assert ((a >= -1) & (a < (1 << 17) * world)).all()
+
+
+def test_pairs_random(rts):
+    rng = np.random.default_rng(21)
+    for world, kc, k in ((8, 2048, 2048), (4, 512, 512), (3, 100, 64), (2, 64, 1000)):
+        rows = 30
+        p = np.zeros((world, rows, kc, 2), np.int32)
+        v = rng.standard_normal((world, rows, kc)).astype(np.float32)
+        v[rng.random(v.shape) < 0.01] = np.nan
+        v[rng.random(v.shape) < 0.01] = -0.0
+        v[rng.random(v.shape) < 0.01] = 0.0
+        v[rng.random(v.shape) < 0.05] = 1.5          # ties on the score
+        p[..., 0] = v.view(np.int32)
+        gid = np.stack([rng.permutation(1 << 20)[:kc * world].reshape(world, kc) for _ in range(rows)],
+                       axis=1)
+        p[..., 1] = gid
+        p[..., 1][rng.random(v.shape) < 0.05] = -1
+        say("pairs", world, kc, k)
+        got = host(rts.merge_select_pairs_rank_major(dev(p), k))
+        exp = oracle.merge_select_pairs_rank_major(p, k)
+        assert_ids_equal(got, exp, f"pairs {world} {kc} {k}")
+
+
+def test_pack_pairs_random(rts):
+    rng = np.random.default_rng(31)
+    rows, cols, kc = 50, 5000, 256
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[rng.random((rows, cols)) < 0.01] = np.nan
+    idx = rng.integers(-2, cols + 3, size=(rows, kc)).astype(np.int32)
+    ends = rng.integers(0, cols + 1, size=rows).astype(np.int32)
+    say("pack pairs")
+    got = host(rts.pack_pairs(dev(x), dev(idx), 3, 8, row_ends=dev(ends)))
+    exp = oracle.pack_pairs(x, idx, 3, 8, ends)
+    assert np.array_equal(got, exp)
+
+
+def test_merge_workload_pipeline_sampled(rts):
+    # Global 6710 x 131072 N(0,1) logits; rank r owns columns g % 8 == r.  GPU:
+    # local top-384 (bf16) -> pack -> rank-major [8, 6710, 396] -> select top-2048.
+    # Pair variant: local top-2048 (fp32) -> pairs [8, 6710, 2048, 2] -> select.
+    W, R, S, N, K = (datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_LOCAL_COLS,
+                     datagen.MERGE_N, datagen.MERGE_K)
+    say("merge workload: generate")
+    g32 = datagen.merge_global()
+    ranks32 = datagen.rank_slices(g32, W)
+    del g32
+    ranks16 = datagen.bf16_bits(ranks32)
+    say("merge workload: gpu")
+    x16 = bf16_dev(ranks16)
+    gathered = torch.empty((W, R, N + N // 32), dtype=torch.int32, device="cuda")
+    locs = []
+    for r in range(W):
+        loc = rts.topk_rows(x16[r], N)
+        locs.append(loc)
+        rts.pack_candidates(x16[r], loc, out=gathered[r])
+    ids, sat = rts.merge_select_rank_major(gathered, K)
+    x32 = dev(ranks32)
+    pairs = torch.empty((W, R, K, 2), dtype=torch.int32, device="cuda")
+    for r in range(W):
+        loc2 = rts.topk_rows(x32[r], K)
+        rts.pack_pairs(x32[r], loc2, r, W, out=pairs[r])
+    pids = rts.merge_select_pairs_rank_major(pairs, K)
+    ids, sat, pids = host(ids), host(sat), host(pids)
+    gpu_locs = np.stack([host(l) for l in locs])
+    gpu_packed = host(gathered)
+
+    sample = np.arange(0, R, 53)
+    say("merge workload: oracle on", len(sample), "rows")
+    o_packed = np.stack([oracle.pack_candidates(ranks16[r][sample],
+                                                oracle.topk_rows(ranks16[r][sample], None, N))
+                         for r in range(W)])
+    o_locs = np.stack([oracle.topk_rows(ranks16[r][sample], None, N) for r in range(W)])
+    assert_ids_equal(gpu_locs[:, sample].reshape(-1, N), o_locs.reshape(-1, N), "local top-384")
+    assert np.array_equal(gpu_packed[:, sample], o_packed), "packed words"
+    eids, esat = oracle.merge_select_rank_major(o_packed, K)
+    assert_ids_equal(ids[sample], eids, "merged ids")
+    assert np.array_equal(sat[sample], esat), "sat_word"
+    o_pairs = np.stack([oracle.pack_pairs(ranks32[r][sample],
+                                          oracle.topk_rows(ranks32[r][sample], None, K), r, W)
+                        for r in range(W)])
+    assert_ids_equal(pids[sample], oracle.merge_select_pairs_rank_major(o_pairs, K), "pair ids")
+    # Every row: with an empty mask the packed result is the exact bf16 top-K;
+    # the pair result is the exact fp32 top-K of the union (each rank sent its top-K).
+    assert ((sat.view(np.uint32) >> 16) == 0).mean() > 0.99
+    for t in sample[:8]:
+        row = np.empty(W * S, np.float32)
+        for r in range(W):
+            row[r::W] = ranks32[r, t]
+        direct = np.argsort(-row, kind="stable")[:K]
+        assert set(pids[t].tolist()) == set(direct.tolist())

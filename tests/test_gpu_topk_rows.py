@@ -1,0 +1,216 @@
+"""GPU parity of topk_rows against the CPU oracle (bit-exact ids).
+
+Covers the pages' test plan for the prefill selector (empty/short rows, lengths
+around k, full rows, strided output, untouched padding, -1 tails, graph replay
+after updating row ends) plus every special value and adversarial order, and
+the measured workloads at full size (the headline one on sampled rows).
+"""
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+from gpu_common import assert_ids_equal, bf16_dev, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def rts():
+    import row_top_select_amd
+    return row_top_select_amd
+
+
+def run_gpu(rts, x, ends, k, dtype="f32", out_cols=None, workspace="auto"):
+    xt = dev(x) if dtype == "f32" else bf16_dev(x)
+    et = None if ends is None else dev(ends.astype(np.int32))
+    out = None
+    if out_cols is not None:
+        out = torch.full((x.shape[0], out_cols), 777, dtype=torch.int32, device="cuda")
+    res = rts.topk_rows(xt, k, row_ends=et, out=out, workspace=workspace)
+    return host(res)
+
+
+def check(rts, x, ends, k, dtype="f32", what="", **kw):
+    got = run_gpu(rts, x, ends, k, dtype, **kw)
+    exp = oracle.topk_rows(x, ends, k)
+    assert_ids_equal(got[:, :k], exp, what or f"{x.shape} k={k} {dtype}")
+    return got
+
+
+def test_tiny_config(rts):
+    w = datagen.WORKLOADS["tiny"]
+    say("tiny", w)
+    check(rts, datagen.logits(w), datagen.row_ends(w), w.k, what="tiny 64x8192")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [1, 7, 64, 100, 512, 600, 2048])
+def test_random_shapes(rts, dtype, k):
+    rng = np.random.default_rng(1000 + k + (dtype == "bf16"))
+    for trial in range(3):
+        rows = int(rng.integers(1, 40))
+        cols = int(rng.integers(1, 9000))
+        x = rng.standard_normal((rows, cols)).astype(np.float32)
+        ends = rng.integers(-5, cols + 50, size=rows).astype(np.int32)
+        ends[0] = cols
+        if rows > 2:
+            ends[1] = min(k, cols)
+            ends[2] = max(0, min(k - 1, cols))
+        say("random", dtype, k, rows, cols, trial)
+        if dtype == "bf16":
+            check(rts, datagen.bf16_bits(x), ends, k, "bf16")
+        else:
+            check(rts, x, ends, k)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_special_values_and_ties(rts, dtype):
+    rng = np.random.default_rng(5)
+    rows, cols, k = 24, 3000, 256
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e-45, -1e-45, 1.0, -1.0],
+                        np.float32)
+    x = rng.choice(specials, size=(rows, cols))
+    ints = rng.integers(-3, 4, size=(rows, cols)).astype(np.float32)
+    x = np.where(rng.random((rows, cols)) < 0.5, ints, x)
+    ends = rng.integers(0, cols + 1, size=rows).astype(np.int32)
+    say("specials", dtype)
+    if dtype == "bf16":
+        check(rts, datagen.bf16_bits(x), ends, k, "bf16")
+    else:
+        check(rts, x, ends, k)
+
+
+@pytest.mark.parametrize("case", ["ascending", "descending", "equal", "nan", "inf_many",
+                                  "plus100", "times1e-8", "neg"])
+def test_adversarial_rows(rts, case):
+    rows, cols, k = 16, 20000, 512
+    rng = np.random.default_rng(9)
+    base = rng.standard_normal((rows, cols)).astype(np.float32)
+    if case == "ascending":
+        x = np.tile(np.arange(cols, dtype=np.float32), (rows, 1))
+    elif case == "descending":
+        x = np.tile(-np.arange(cols, dtype=np.float32), (rows, 1))
+    elif case == "equal":
+        x = np.full((rows, cols), 2.5, np.float32)
+    elif case == "nan":
+        x = np.full((rows, cols), np.nan, np.float32)
+        x[::2, ::97] = 1.0
+    elif case == "inf_many":
+        x = base.copy()
+        x[rng.random((rows, cols)) < 0.05] = np.inf
+    elif case == "plus100":
+        x = base + np.float32(100.0)
+    elif case == "times1e-8":
+        x = base * np.float32(1e-8)
+    else:
+        x = -np.abs(base)
+    ends = np.full(rows, cols, np.int32)
+    ends[1] = 0
+    ends[2] = 511
+    ends[3] = 513
+    say("adversarial", case)
+    check(rts, x, ends, k, what=case)
+
+
+def test_null_row_ends_strided_io(rts):
+    rng = np.random.default_rng(3)
+    big = rng.standard_normal((33, 5003)).astype(np.float32)
+    x = big[:, 1:4001]                      # misaligned start, ld = 5003
+    k = 300
+    xt = dev(big)[:, 1:4001]
+    out = torch.full((33, k + 13), 777, dtype=torch.int32, device="cuda")
+    say("strided")
+    rts.topk_rows(xt, k, row_ends=None, out=out)
+    got = host(out)
+    assert (got[:, k:] == 777).all(), "columns past k must stay untouched"
+    assert_ids_equal(got[:, :k], oracle.topk_rows(np.ascontiguousarray(x), None, k), "strided")
+
+
+def test_workspace_split_equals_single(rts):
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((8, 60000)).astype(np.float32)
+    ends = np.array([60000, 59999, 0, 1, 511, 512, 513, 40000], np.int32)
+    say("split")
+    a = run_gpu(rts, x, ends, 512, workspace="auto")
+    b = run_gpu(rts, x, ends, 512, workspace=None)
+    exp = oracle.topk_rows(x, ends, 512)
+    assert_ids_equal(a, exp, "split")
+    assert_ids_equal(b, exp, "single")
+
+
+def test_determinism(rts):
+    w = datagen.WORKLOADS["ties"]
+    x = datagen.logits(w, blocks=[0])[:256]
+    ends = datagen.row_ends(w)[:256]
+    xt, et = dev(x), dev(ends)
+    say("determinism")
+    first = host(rts.topk_rows(xt, 512, row_ends=et))
+    for _ in range(5):
+        assert np.array_equal(host(rts.topk_rows(xt, 512, row_ends=et)), first)
+
+
+def test_graph_replay_after_updating_row_ends(rts):
+    rng = np.random.default_rng(8)
+    rows, cols, k = 64, 9000, 512
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    xt = dev(x)
+    et = dev(np.full(rows, cols, np.int32))
+    out = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    rts.topk_rows(xt, k, row_ends=et, out=out)      # warm up outside capture
+    torch.cuda.synchronize()
+    say("graph capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rts.topk_rows(xt, k, row_ends=et, out=out)
+    for trial in range(4):
+        ends = rng.integers(-2, cols + 2, size=rows).astype(np.int32)
+        et.copy_(torch.from_numpy(ends))
+        torch.cuda.synchronize()
+        g.replay()
+        got = host(out)
+        assert_ids_equal(got, oracle.topk_rows(x, ends, k), f"replay {trial}")
+        rts.topk_rows(xt, 3, row_ends=et)             # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["prefill", "ties", "long"])
+def test_full_size_configs(rts, name):
+    w = datagen.WORKLOADS[name]
+    say("full", w)
+    x = datagen.logits(w)
+    ends = datagen.row_ends(w)
+    got = run_gpu(rts, x, ends, w.k)
+    exp = oracle.topk_rows(x, ends, w.k)
+    assert_ids_equal(got, exp, name)
+
+
+def test_decode_config(rts):
+    w = datagen.WORKLOADS["decode"]
+    say("decode", w)
+    x = datagen.logits(w)
+    ends = datagen.row_ends(w)
+    assert_ids_equal(run_gpu(rts, x, ends, w.k), oracle.topk_rows(x, ends, w.k), "decode")
+
+
+def test_verylong_config_sampled(rts):
+    # The headline workload at full size, launched as the benchmark launches it;
+    # the oracle checks 128 rows spread over all four 1024-row blocks.
+    w = datagen.WORKLOADS["verylong"]
+    say("verylong generate")
+    x = datagen.logits(w)
+    ends = datagen.row_ends(w)
+    xt, et = dev(x), dev(ends)
+    say("verylong run")
+    got = host(rts.topk_rows(xt, w.k, row_ends=et))
+    sample = np.arange(0, w.rows, 32)
+    exp = oracle.topk_rows(x[sample], ends[sample], w.k)
+    assert_ids_equal(got[sample], exp, "verylong sampled rows")
+    # properties on every row: ids unique, inside the row, descending scores
+    assert (got >= 0).all()
+    assert (got < ends[:, None]).all()
+    vals = np.take_along_axis(x, got.astype(np.int64), axis=1)
+    assert (np.diff(vals, axis=1) <= 0).all()
