@@ -1,0 +1,229 @@
+"""Benchmark of the row top-K select on one MI355X.
+
+Headline workload: top-512 of every row of a 4096 x 102400 fp32 logit matrix
+(N(0,1), seed 105) with causal row ends row_end[i] = 98305 + i, the pages'
+"very long rows" synthetic control.  One step = one topk_rows call over the
+whole matrix, inputs resident in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--all] [--copy-calib]
+
+--all adds the other workloads (prefill, ties, long, decode, packed and pair
+merges) as a "secondary" object; --copy-calib only runs a plain 1 GiB device
+copy (the reference point for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0                  # MI355X HBM3E
+PAGES_ROWS_PER_S = 4096 / 499.9e-6     # best published rate on this workload (GB200, context)
+COUNTERS = os.path.join(ROOT, "profiles", "topk_rows_verylong_counters.json")
+KERNEL_SOURCES = ["row_top_select_amd/csrc/rts_topk_rows.hip",
+                  "row_top_select_amd/csrc/rts_device.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(ends, k, rows, elem=4) -> int:
+    # logits inside [0, row_end) + row_ends + k int32 ids per row
+    return int(ends.astype("int64").sum()) * elem + rows * 4 + rows * k * 4
+
+
+def time_calls(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, ev0.elapsed_time(ev1) / 1e3 / steps
+
+
+def cpu_baseline(x_sample, ends_sample, k, total_rows_note):
+    import oracle
+    t0 = time.perf_counter()
+    ids = oracle.topk_rows(x_sample, ends_sample, k)
+    dt = time.perf_counter() - t0
+    return ids, {
+        "value": x_sample.shape[0] / dt,
+        "unit": "rows/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"{x_sample.shape[0]} of {total_rows_note} rows (rows 0..{x_sample.shape[0] - 1}, "
+                  f"same data and row ends), one run, {dt:.2f} s wall",
+    }
+
+
+def secondary(torch, rts, datagen, steps, warmup):
+    import numpy as np
+    res = {}
+    for name in ("prefill", "ties", "long", "decode"):
+        w = datagen.WORKLOADS[name]
+        x = torch.from_numpy(datagen.logits(w)).cuda()
+        ends_np = datagen.row_ends(w)
+        ends = torch.from_numpy(ends_np).cuda()
+        out = torch.empty((w.rows, w.k), dtype=torch.int32, device="cuda")
+        ws_n = rts.topk_rows_workspace_size(torch.float32, w.rows, w.cols, w.k)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+        _, t = time_calls(lambda: rts.topk_rows(x, w.k, row_ends=ends, out=out,
+                                                workspace=ws if ws_n else None),
+                          steps, warmup, torch)
+        b = algorithmic_bytes(ends_np, w.k, w.rows)
+        res[name] = {"shape": [w.rows, w.cols], "k": w.k, "us_per_call": t * 1e6,
+                     "rows_per_s": w.rows / t, "algorithmic_GBps": b / t / 1e9}
+        del x
+    # Packed merge (config of 8 simulated ranks) and the pair merge.
+    W, R, S, N, K = (datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_LOCAL_COLS,
+                     datagen.MERGE_N, datagen.MERGE_K)
+    g = datagen.merge_global()
+    ranks32 = datagen.rank_slices(g, W)
+    del g
+    x16 = torch.from_numpy(datagen.bf16_bits(ranks32).view(np.int16)).cuda().view(torch.bfloat16)
+    gathered = torch.empty((W, R, N + N // 32), dtype=torch.int32, device="cuda")
+    locs = [rts.topk_rows(x16[r], N) for r in range(W)]
+    _, t_local = time_calls(lambda: rts.topk_rows(x16[0], N, out=locs[0]), steps, warmup, torch)
+    _, t_pack = time_calls(lambda: rts.pack_candidates(x16[0], locs[0], out=gathered[0]), steps,
+                           warmup, torch)
+    for r in range(1, W):
+        rts.pack_candidates(x16[r], locs[r], out=gathered[r])
+    ids = torch.empty((R, K), dtype=torch.int32, device="cuda")
+    sat = torch.empty((R,), dtype=torch.int32, device="cuda")
+    _, t_sel = time_calls(lambda: rts.merge_select_rank_major(gathered, K, out=ids, sat_word=sat),
+                          steps, warmup, torch)
+    sel_bytes = W * R * (N + N // 32) * 4 + R * K * 4 + R * 4
+    res["merge_packed"] = {"shape": [W, R, N + N // 32], "k": K,
+                           "select_us": t_sel * 1e6, "select_rows_per_s": R / t_sel,
+                           "select_algorithmic_GBps": sel_bytes / t_sel / 1e9,
+                           "local_top384_bf16_us_per_rank": t_local * 1e6,
+                           "pack_us_per_rank": t_pack * 1e6}
+    del x16
+    x32 = torch.from_numpy(ranks32).cuda()
+    del ranks32
+    pairs = torch.empty((W, R, K, 2), dtype=torch.int32, device="cuda")
+    for r in range(W):
+        rts.pack_pairs(x32[r], rts.topk_rows(x32[r], K), r, W, out=pairs[r])
+    pid = torch.empty((R, K), dtype=torch.int32, device="cuda")
+    _, t_pairs = time_calls(lambda: rts.merge_select_pairs_rank_major(pairs, K, out=pid), steps,
+                            warmup, torch)
+    pb = W * R * K * 8 + R * K * 4
+    res["merge_pairs"] = {"shape": [W, R, K, 2], "k": K, "select_us": t_pairs * 1e6,
+                          "select_rows_per_s": R / t_pairs,
+                          "select_algorithmic_GBps": pb / t_pairs / 1e9}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--all", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
+              f"{args.gpus}); rows shard across GPUs with no exchange, so run one process per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calib:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "calls": 3}))
+        return
+
+    import datagen
+    import row_top_select_amd as rts
+
+    w = datagen.WORKLOADS["verylong"]
+    x_np = datagen.logits(w, threads=8)
+    ends_np = datagen.row_ends(w)
+    x = torch.from_numpy(x_np).cuda()
+    ends = torch.from_numpy(ends_np).cuda()
+    out = torch.empty((w.rows, w.k), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        rts.topk_rows(x, w.k, row_ends=ends, out=out, workspace=None)
+
+    wall, t_kernel = time_calls(step, args.steps, args.warmup, torch)
+    ms_per_step = wall / args.steps * 1e3
+    value = w.rows * args.steps / wall
+    abytes = algorithmic_bytes(ends_np, w.k, w.rows)
+    achieved = abytes / t_kernel / 1e9
+
+    traffic = None
+    if os.path.exists(COUNTERS):
+        c = json.load(open(COUNTERS))
+        if c.get("kernel_source_hash") == kernel_source_hash():
+            traffic = c.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": "rows/s and achieved HBM GB/s, top-512 select at 4096×102400 fp32",
+        "value": value,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": value / PAGES_ROWS_PER_S,
+        "vs_baseline_note": "ratio to 4096 rows / 499.9 us, the best published figure on this "
+                            "workload (DeepSelect on one GB200): context, another machine",
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "topk512_rows4096_cols102400_f32_causal", "rows": w.rows,
+                   "cols": w.cols, "k": w.k, "row_ends": "98305+i", "distribution": "N(0,1)",
+                   "seed": w.seed},
+        "us_per_call": t_kernel * 1e6,
+        "achieved_GBps": achieved,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes": abytes},
+    }
+    if not args.no_cpu:
+        sample = 1024
+        ids, cpu = cpu_baseline(x_np[:sample], ends_np[:sample], w.k, w.rows)
+        result["cpu_baseline"] = cpu
+        result["parity_sample_rows_equal"] = bool(np.array_equal(out[:sample].cpu().numpy(), ids))
+    if args.all:
+        del x
+        torch.cuda.empty_cache()
+        result["secondary"] = secondary(torch, rts, datagen, max(5, args.steps // 5), 2)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
