@@ -46,10 +46,56 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// ---------------------------------------------------------------------------
+// Lane exchange and reductions.  DPP (row/quad permutes, row broadcasts) and
+// ds_swizzle stay out of LDS memory; only a lane xor of 32 uses ds_bpermute.
+// DPP control codes of the GFX9 encoding.
+// ---------------------------------------------------------------------------
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowShl4 = 0x104;  // lane i <- lane i+4 (same row of 16)
+constexpr int kDppRowShr1 = 0x111;  // lane i <- lane i-1
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowRor8 = 0x128;  // lane i <- lane (i+8) mod 16
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND = false>
+__device__ __forceinline__ uint32_t dpp32(uint32_t old, uint32_t src) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, ROW_MASK, 0xF, BOUND);
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp64(uint64_t old, uint64_t src) {
+    const uint32_t lo = dpp32<CTRL, ROW_MASK>((uint32_t)old, (uint32_t)src);
+    const uint32_t hi = dpp32<CTRL, ROW_MASK>((uint32_t)(old >> 32), (uint32_t)(src >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// v of lane (lane ^ lj), for lj a power of two below 64.
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t v, int lj) {
+    switch (lj) {
+        case 1: return dpp32<kDppQuadXor1>(v, v);
+        case 2: return dpp32<kDppQuadXor2>(v, v);
+        case 4: {
+            const uint32_t up = dpp32<kDppRowShl4>(v, v);
+            const uint32_t dn = dpp32<kDppRowShr4>(v, v);
+            return (__lane_id() & 4) ? dn : up;
+        }
+        case 8: return dpp32<kDppRowRor8>(v, v);
+        case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+        default: return (uint32_t)__shfl_xor((int)v, lj, kWave);
+    }
+}
+
 __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int mask) {
-    int lo = __shfl_xor((int)(uint32_t)v, mask, kWave);
-    int hi = __shfl_xor((int)(uint32_t)(v >> 32), mask, kWave);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+    const uint32_t lo = lane_xor32((uint32_t)v, mask);
+    const uint32_t hi = lane_xor32((uint32_t)(v >> 32), mask);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
@@ -122,46 +168,53 @@ __device__ __forceinline__ void wave_bitonic_merge(uint64_t (&v)[N]) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave reductions
+// Wave reductions (result uniform, read from lane 63) and inclusive scan.
+// Steps: quad xor 1 and 2, half-row and row mirrors (each row of 16 then holds
+// its total), row 15 -> rows 1/3, lane 31 -> rows 2/3.
 // ---------------------------------------------------------------------------
+template <typename Op>
+__device__ __forceinline__ uint64_t wave_reduce64(uint64_t v, Op op) {
+    v = op(v, dpp64<kDppQuadXor1>(v, v));
+    v = op(v, dpp64<kDppQuadXor2>(v, v));
+    v = op(v, dpp64<kDppRowHalfMirror>(v, v));
+    v = op(v, dpp64<kDppRowMirror>(v, v));
+    v = op(v, dpp64<kDppRowBcast15, 0xA>(v, v));
+    v = op(v, dpp64<kDppRowBcast31, 0xC>(v, v));
+    return readlane64(v, kWave - 1);
+}
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce32(uint32_t v, Op op) {
+    v = op(v, dpp32<kDppQuadXor1>(v, v));
+    v = op(v, dpp32<kDppQuadXor2>(v, v));
+    v = op(v, dpp32<kDppRowHalfMirror>(v, v));
+    v = op(v, dpp32<kDppRowMirror>(v, v));
+    v = op(v, dpp32<kDppRowBcast15, 0xA>(v, v));
+    v = op(v, dpp32<kDppRowBcast31, 0xC>(v, v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
 __device__ __forceinline__ uint32_t wave_sum32(uint32_t v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v += (uint32_t)__shfl_xor((int)v, d, kWave);
-    return v;
+    return wave_reduce32(v, [](uint32_t a, uint32_t b) { return a + b; });
 }
-
 __device__ __forceinline__ uint32_t wave_or32(uint32_t v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v |= (uint32_t)__shfl_xor((int)v, d, kWave);
-    return v;
+    return wave_reduce32(v, [](uint32_t a, uint32_t b) { return a | b; });
 }
-
-__device__ __forceinline__ uint64_t wave_and64(uint64_t v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v &= shfl_xor64(v, d);
-    return v;
-}
-
-__device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v |= shfl_xor64(v, d);
-    return v;
-}
-
 __device__ __forceinline__ uint64_t wave_min64(uint64_t v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v = umin64(v, shfl_xor64(v, d));
-    return v;
+    return wave_reduce64(v, [](uint64_t a, uint64_t b) { return umin64(a, b); });
+}
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+    return wave_reduce64(v, [](uint64_t a, uint64_t b) { return umax64(a, b); });
 }
 
-// Inclusive prefix sum over one wave.
+// Inclusive prefix sum over the wave (lane order).
 __device__ __forceinline__ uint32_t wave_incl_scan32(uint32_t v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        uint32_t t = (uint32_t)__shfl_up((int)v, d, kWave);
-        if (lane >= d) v += t;
-    }
+    v += dpp32<kDppRowShr1, 0xF, true>(0u, v);
+    v += dpp32<kDppRowShr2, 0xF, true>(0u, v);
+    v += dpp32<kDppRowShr4, 0xF, true>(0u, v);
+    v += dpp32<kDppRowShr8, 0xF, true>(0u, v);
+    v += dpp32<kDppRowBcast15, 0xA>(0u, v);
+    v += dpp32<kDppRowBcast31, 0xC>(0u, v);
     return v;
 }
 

@@ -96,8 +96,7 @@ __device__ uint64_t block_radix_kth(const uint64_t (&key)[KPT], int k, SelectSme
             mx = in ? umax64(mx, key[i]) : mx;
         }
         mn = wave_min64(mn);
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) mx = umax64(mx, shfl_xor64(mx, d));
+        mx = wave_max64(mx);
         if (lane == 0) {
             sm.red_lo[wave] = mn;
             sm.red_hi[wave] = mx;

@@ -16,7 +16,7 @@
 //     tie has a larger id and loses), so the filter is one float compare per
 //     element against the float whose key is tau + 1; NaN fails every compare.
 //   * Survivors are appended to a wave-private LDS stage (ballot + lane prefix
-//     count).  When the stage cannot take another chunk, a wave-level radix
+//     count).  When the stage cannot take another 64 survivors, a wave-level radix
 //     select finds the exact k-th composite among the staged entries and keeps
 //     only the top k.  Its digit window is relative to [min, max] of the keys
 //     still in play, so concentrated score distributions do not pile into one
@@ -78,92 +78,109 @@ __device__ __forceinline__ void unpack(typename RowTraits<BF16>::vec v, uint32_t
     }
 }
 
-__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+// One level of the wave radix select: bins of [mn, mx] of the composites in
+// [lo_edge, hi_edge] (all nonzero ones on the first level).  Returns true when
+// done, with *T set; otherwise narrows [lo_edge, hi_edge] and need.
+template <int NV, bool FIRST>
+__device__ __forceinline__ bool wave_radix_level(const uint64_t (&v)[NV], uint64_t& lo_edge,
+                                                 uint64_t& hi_edge, int& need, uint64_t* T,
+                                                 uint32_t* hist, bool force_end) {
+    const int lane = lane_id();
+    uint64_t mn = ~0ull, mx = 0;
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v = umax64(v, shfl_xor64(v, d));
-    return v;
+    for (int r = 0; r < NV; ++r) {
+        const bool in = FIRST ? v[r] != 0ull : (v[r] >= lo_edge && v[r] <= hi_edge);
+        mn = in ? umin64(mn, v[r]) : mn;
+        mx = in ? umax64(mx, v[r]) : mx;
+    }
+    mn = wave_min64(mn);
+    mx = wave_max64(mx);
+    if (mn == mx) {
+        *T = mn;
+        return true;
+    }
+    const uint64_t d = mx - mn;
+    const int bl = 64 - __clzll((long long)d);
+    const int s = bl > 8 ? bl - 8 : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
+    wave_lds_sync();
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+        const bool in = FIRST ? v[r] != 0ull : (v[r] >= lo_edge && v[r] <= hi_edge);
+        if (in)
+            __hip_atomic_fetch_add(&hist[(uint32_t)((v[r] - mn) >> s)], 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WAVEFRONT);
+    }
+    wave_lds_sync();
+    // Lane l owns bins 255-4l .. 252-4l, scanned from the top.
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = hist[255 - 4 * lane - j];
+    const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+    uint32_t run = wave_incl_scan32(tot) - tot;
+    int fj = -1;
+    uint32_t above = 0, cb = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (fj < 0 && run < (uint32_t)need && run + c[j] >= (uint32_t)need) {
+            fj = j;
+            above = run;
+            cb = c[j];
+        }
+        run += c[j];
+    }
+    wave_lds_sync();
+    const uint64_t fm = __ballot(fj >= 0);
+    if (fm == 0ull || force_end) {  // only if the count invariant were broken
+        *T = mn;
+        return true;
+    }
+    const int fl = __ffsll((long long)fm) - 1;
+    const int bj = __builtin_amdgcn_readlane(fj, fl);
+    above = __builtin_amdgcn_readlane(above, fl);
+    cb = __builtin_amdgcn_readlane(cb, fl);
+    const uint32_t bin = 255u - 4u * (uint32_t)fl - (uint32_t)bj;
+    need -= (int)above;
+    const uint64_t blo = mn + ((uint64_t)bin << s);
+    if ((int)cb == need) {
+        *T = blo;
+        return true;
+    }
+    lo_edge = blo;
+    // The top bin ends at mx (blo + 2^s - 1 could wrap past 2^64 there).
+    hi_edge = bin == (uint32_t)(d >> s) ? mx : blo + ((1ull << s) - 1ull);
+    return false;
 }
 
 // Exact k-th largest composite among v[] (0 = empty); requires k <= number of
 // nonzero entries.  Returns T such that exactly k nonzero entries are >= T
-// when composites are distinct.  hist: 256 wave-private LDS counters.
-template <int ES>
-__device__ __forceinline__ uint64_t wave_radix_kth(const uint64_t (&v)[ES], int k, uint32_t* hist) {
-    const int lane = lane_id();
-    uint64_t lo_edge = 1, hi_edge = ~0ull;
+// when composites are distinct.  hist: 256 wave-private LDS counters.  Each
+// level narrows the range by at least 2^7, so 10 levels always finish; the
+// cap only bounds the loop if the count invariant were ever broken.
+template <int NV>
+__device__ __forceinline__ uint64_t wave_radix_kth(const uint64_t (&v)[NV], int k, uint32_t* hist) {
+    uint64_t lo_edge = 1, hi_edge = ~0ull, T = 0;
     int need = k;
-    // Each level narrows the range by at least 2^7, so 10 levels always finish;
-    // the cap only bounds the loop if the count invariant were ever broken.
-    for (int level = 0;; ++level) {
-        uint64_t mn = ~0ull, mx = 0;
-#pragma unroll
-        for (int r = 0; r < ES; ++r) {
-            const bool in = v[r] >= lo_edge && v[r] <= hi_edge;
-            mn = in ? umin64(mn, v[r]) : mn;
-            mx = in ? umax64(mx, v[r]) : mx;
-        }
-        mn = wave_min64(mn);
-        mx = wave_max64(mx);
-        if (mn == mx) return mn;
-        const uint64_t d = mx - mn;
-        const int bl = 64 - __clzll((long long)d);
-        const int s = bl > 8 ? bl - 8 : 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
-        wave_lds_sync();
-#pragma unroll
-        for (int r = 0; r < ES; ++r) {
-            if (v[r] >= lo_edge && v[r] <= hi_edge)
-                __hip_atomic_fetch_add(&hist[(uint32_t)((v[r] - mn) >> s)], 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WAVEFRONT);
-        }
-        wave_lds_sync();
-        // Lane l owns bins 255-4l .. 252-4l, scanned from the top.
-        uint32_t c[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) c[j] = hist[255 - 4 * lane - j];
-        const uint32_t tot = c[0] + c[1] + c[2] + c[3];
-        uint32_t run = wave_incl_scan32(tot) - tot;
-        int fj = -1;
-        uint32_t above = 0, cb = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (fj < 0 && run < (uint32_t)need && run + c[j] >= (uint32_t)need) {
-                fj = j;
-                above = run;
-                cb = c[j];
-            }
-            run += c[j];
-        }
-        wave_lds_sync();
-        const uint64_t fm = __ballot(fj >= 0);
-        if (fm == 0ull || level >= 12) return mn;
-        const int fl = __ffsll((long long)fm) - 1;
-        const int bj = __builtin_amdgcn_readlane(fj, fl);
-        above = __builtin_amdgcn_readlane(above, fl);
-        cb = __builtin_amdgcn_readlane(cb, fl);
-        const uint32_t bin = 255u - 4u * (uint32_t)fl - (uint32_t)bj;
-        need -= (int)above;
-        const uint64_t blo = mn + ((uint64_t)bin << s);
-        if ((int)cb == need) return blo;
-        lo_edge = blo;
-        // The top bin ends at mx (blo + 2^s - 1 could wrap past 2^64 there).
-        hi_edge = bin == (uint32_t)(d >> s) ? mx : blo + ((1ull << s) - 1ull);
-    }
+    if (wave_radix_level<NV, true>(v, lo_edge, hi_edge, need, &T, hist, false)) return T;
+    for (int level = 1;; ++level)
+        if (wave_radix_level<NV, false>(v, lo_edge, hi_edge, need, &T, hist, level >= 12)) return T;
 }
 
 template <int E, int ES, bool BF16, int P>
-__global__ __launch_bounds__(kWave* P) void topk_rows_stream_kernel(
+__global__ __launch_bounds__(kWave* P) __attribute__((amdgpu_waves_per_eu(E <= 8 ? 4 : 2)))
+void topk_rows_stream_kernel(
     const void* __restrict__ xv, int64_t cols, int64_t ld, const int32_t* __restrict__ row_ends,
     int32_t k, int32_t* __restrict__ out, int64_t ld_out, uint64_t* __restrict__ part,
     int32_t groups) {
     using T = typename RowTraits<BF16>::elem;
     using V = typename RowTraits<BF16>::vec;
     constexpr int LP = kWave * E;
-    constexpr int SCAP = kWave * ES;
-    static_assert(SCAP >= LP + kChunk, "stage must hold the list and one chunk");
+    constexpr int SCAP = kWave * ES;            // room for new survivors
+    constexpr int SBUF = SCAP > LP ? SCAP : LP;  // also carries the selected list into L
+    static_assert(SCAP >= kChunk, "the stage must take a whole chunk");
 
-    __shared__ uint64_t stage_all[P][SCAP];
+    __shared__ uint64_t stage_all[P][SBUF];
     __shared__ uint32_t hist_all[P][256];
     __shared__ uint32_t thr_shared;
 
@@ -193,8 +210,13 @@ __global__ __launch_bounds__(kWave* P) void topk_rows_stream_kernel(
     const T* rowp = reinterpret_cast<const T*>(xv) + row * ld;
 
     int cnt = 0;                     // staged entries (wave-uniform)
+    int nl = 0;                      // entries in the register list L (wave-uniform)
     uint32_t thr_own = 0x007FFFFFu;  // key of -inf: every non-NaN value passes
     float f = float_of_key32(thr_own);
+    // The current top list: up to k composites, E per lane, unsorted.
+    uint64_t L[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) L[r] = 0;
 
     auto refresh = [&]() {
         uint32_t t = thr_own;
@@ -217,24 +239,6 @@ __global__ __launch_bounds__(kWave* P) void topk_rows_stream_kernel(
         if (m) append(m, bits, col);
     };
 
-    // One chunk: columns col0 .. col0+3 of each lane; needs kChunk free slots.
-    auto process = [&](V vv, uint32_t col0) {
-        uint32_t bits[kVec];
-        unpack<BF16>(vv, bits);
-        uint64_t m[kVec];
-        uint64_t any = 0;
-#pragma unroll
-        for (int c = 0; c < kVec; ++c) {
-            m[c] = __ballot(__uint_as_float(bits[c]) >= f);
-            any |= m[c];
-        }
-        if (any) {
-#pragma unroll
-            for (int c = 0; c < kVec; ++c)
-                if (m[c]) append(m[c], bits[c], col0 + (uint32_t)c);
-        }
-    };
-
     // Geometry: head [a, a1) up to the first aligned vector, body of whole
     // chunks, tail [t0, b).
     int64_t a1 = a, nch = 0, t0 = a;
@@ -249,6 +253,8 @@ __global__ __launch_bounds__(kWave* P) void topk_rows_stream_kernel(
     }
     const V* bp = reinterpret_cast<const V*>(rowp + a1) + lane;
     const int64_t ngroups = (nch + kGroup - 1) / kGroup;
+
+    __builtin_amdgcn_s_setprio(3);
 
     // Head: fewer than kVec elements, the stage is empty.
     if (a1 > a) {
@@ -271,23 +277,64 @@ __global__ __launch_bounds__(kWave* P) void topk_rows_stream_kernel(
         load_group(A, 0);
         load_group(B, ngroups > 1 ? 1 : 0);
     }
-    int ustart = 0;
+    int ustart = 0;  // first chunk of the group still to process
+    // A chunk interrupted by a full stage: its masks (taken against the older,
+    // lower threshold: a superset) and values; finished right after the
+    // compaction.  Re-filtering it strictly could drop a tie whose id is smaller
+    // than that of an entry of the same chunk already in the list.
+    bool pend = false;
+    int pend_c = 0;
+    uint32_t pbits[kVec] = {0, 0, 0, 0};
+    uint64_t pm[kVec] = {0, 0, 0, 0};
+    uint32_t pcol0 = 0;
     int64_t tpos = t0;
     int phase = ngroups > 0 ? 0 : 1;  // 0 body, 1 tail, 2 end
+
+    // One chunk: returns false (after saving the rest as pending) if the stage
+    // filled up inside it.
+    auto chunk = [&](V vv, uint32_t col0, int u) -> bool {
+        uint32_t bits[kVec];
+        unpack<BF16>(vv, bits);
+        uint64_t m[kVec];
+#pragma unroll
+        for (int c = 0; c < kVec; ++c) m[c] = __ballot(__uint_as_float(bits[c]) >= f);
+        if ((m[0] | m[1] | m[2] | m[3]) == 0ull) return true;
+#pragma unroll
+        for (int c = 0; c < kVec; ++c) {
+            if (m[c]) {
+                if (cnt + kWave > SCAP) {
+                    pend = true;
+                    pend_c = c;
+                    pcol0 = col0;
+#pragma unroll
+                    for (int q = 0; q < kVec; ++q) {
+                        pbits[q] = bits[q];
+                        pm[q] = m[q];
+                    }
+                    ustart = u + 1;
+                    return false;
+                }
+                append(m[c], bits[c], col0 + (uint32_t)c);
+            }
+        }
+        return true;
+    };
 
     for (;;) {
         bool need = false;
         if (phase == 0) {
             while (true) {
+                if (ustart == 0 && (gi + 1) * kGroup <= nch) {
 #pragma unroll
-                for (int u = 0; u < kGroup; ++u) {
-                    if (!need && u >= ustart && gi * kGroup + u < nch) {
-                        if (cnt + kChunk > SCAP) {
-                            need = true;
-                            ustart = u;
-                        } else {
-                            process(A[u], (uint32_t)(a1 + (gi * kGroup + u) * kChunk + lane * kVec));
-                        }
+                    for (int u = 0; u < kGroup; ++u) {
+                        if (!need)
+                            need = !chunk(A[u], (uint32_t)(a1 + (gi * kGroup + u) * kChunk + lane * kVec), u);
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < kGroup; ++u) {
+                        if (!need && u >= ustart && gi * kGroup + u < nch)
+                            need = !chunk(A[u], (uint32_t)(a1 + (gi * kGroup + u) * kChunk + lane * kVec), u);
                     }
                 }
                 if (need) break;
@@ -301,6 +348,17 @@ __global__ __launch_bounds__(kWave* P) void topk_rows_stream_kernel(
                 for (int u = 0; u < kGroup; ++u) A[u] = B[u];
                 load_group(B, gi + 1 < ngroups ? gi + 1 : gi);
                 if constexpr (P > 1) refresh();
+                // The SIMD issues the oldest ready wave first, so waves that started
+                // later fall behind once their compactions compete for issue slots.
+                // A wave lowers its priority as it advances through its piece, so
+                // the ones behind win instead and all finish together.
+                if ((gi & 7) == 0) {
+                    const int64_t q = (gi * 4) / ngroups;
+                    if (q == 0) __builtin_amdgcn_s_setprio(3);
+                    else if (q == 1) __builtin_amdgcn_s_setprio(2);
+                    else if (q == 2) __builtin_amdgcn_s_setprio(1);
+                    else __builtin_amdgcn_s_setprio(0);
+                }
             }
         }
         if (!need && phase == 1) {
@@ -316,49 +374,61 @@ __global__ __launch_bounds__(kWave* P) void topk_rows_stream_kernel(
             }
             if (!need) phase = 2;
         }
-        if (!need && phase == 2 && cnt <= k) break;
+        if (!need && phase == 2 && cnt == 0) break;
 
-        // Compaction (single call site): keep the exact top-k of the stage.
+        // Compaction (single call site): L <- exact top-k of L and the stage.
         wave_lds_sync();
-        uint64_t v[ES];
+        uint64_t v[E + ES];
+#pragma unroll
+        for (int r = 0; r < E; ++r) v[r] = L[r];
 #pragma unroll
         for (int r = 0; r < ES; ++r) {
             const int idx = r * kWave + lane;
-            v[r] = idx < cnt ? stage[idx] : 0ull;
+            v[E + r] = idx < cnt ? stage[idx] : 0ull;
         }
-        const uint64_t T0 = wave_radix_kth<ES>(v, k, hist);
+        const uint64_t T0 = nl + cnt > k ? wave_radix_kth<E + ES>(v, k, hist) : 1ull;
         wave_lds_sync();
         int base = 0;
         uint64_t kth = ~0ull;
 #pragma unroll
-        for (int r = 0; r < ES; ++r) {
+        for (int r = 0; r < E + ES; ++r) {
             const bool sel = v[r] != 0ull && v[r] >= T0;
             const uint64_t m = __ballot(sel);
             if (sel) stage[base + (int)mbcnt64(m)] = v[r];
             base += (int)__popcll(m);
             kth = sel ? umin64(kth, v[r]) : kth;
         }
-        kth = wave_min64(kth);
-        // Distinct composites leave exactly k; never let the stage stay full.
-        cnt = base <= SCAP - kChunk ? base : SCAP - kChunk;
-        thr_own = (uint32_t)(kth >> 32) + 1u;
-        if constexpr (P > 1) {
-            if (lane == 0)
-                __hip_atomic_fetch_max(&thr_shared, (uint32_t)(kth >> 32), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+        // Distinct composites leave at most k; never exceed the list.
+        nl = base < LP ? base : LP;
+        wave_lds_sync();
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+            const int idx = lane * E + r;
+            L[r] = idx < nl ? stage[idx] : 0ull;
+        }
+        wave_lds_sync();
+        cnt = 0;
+        if (nl >= k) {
+            kth = wave_min64(kth);
+            thr_own = (uint32_t)(kth >> 32) + 1u;
+            if constexpr (P > 1) {
+                if (lane == 0)
+                    __hip_atomic_fetch_max(&thr_shared, (uint32_t)(kth >> 32), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
         }
         refresh();
-        if (phase == 2) break;
+        if (pend) {
+            // The stage is empty now, so the rest of the chunk fits.
+#pragma unroll
+            for (int c = 0; c < kVec; ++c)
+                if (c >= pend_c && pm[c]) append(pm[c], pbits[c], pcol0 + (uint32_t)c);
+            pend = false;
+        }
+        if (phase == 2 && cnt == 0) break;
     }
 
     // The wave's top list, sorted descending, blocked (lane l: l*E .. l*E+E-1).
-    wave_lds_sync();
-    uint64_t L[E];
-#pragma unroll
-    for (int r = 0; r < E; ++r) {
-        const int idx = lane * E + r;
-        L[r] = idx < cnt ? stage[idx] : 0ull;
-    }
     wave_bitonic_sort<E, true>(L);
 
     // Workgroup: merge the waves' lists pairwise (stage memory is reused).
@@ -451,8 +521,8 @@ int list_e(int32_t k) {
     return e;
 }
 
-// Stage entries per lane: the list (E per lane) plus room for several chunks.
-constexpr int stage_es(int e) { return e >= 32 ? 40 : e + (e > 8 ? e : 8); }
+// Stage entries per lane (new survivors between two compactions).
+constexpr int stage_es(int e) { return e <= 4 ? e + 8 : (e <= 16 ? 16 : 8); }
 
 template <int E, bool BF16, int P>
 void launch_stream(const void* x, int64_t rows, int64_t cols, int64_t ld, const int32_t* re,
