@@ -228,8 +228,10 @@ void topk_rows_stream_kernel(
         f = float_of_key32(t);
     };
 
+    // Staged entries hold the raw score bits in the high word (the key transform
+    // is applied once per entry when the stage is compacted).
     auto append = [&](uint64_t m, uint32_t bits, uint32_t col) {
-        if ((m >> lane) & 1ull) stage[cnt + (int)mbcnt64(m)] = composite(key32_of_bits(bits), col);
+        if ((m >> lane) & 1ull) stage[cnt + (int)mbcnt64(m)] = composite(bits, col);
         cnt += (int)__popcll(m);
     };
 
@@ -254,6 +256,17 @@ void topk_rows_stream_kernel(
     const V* bp = reinterpret_cast<const V*>(rowp + a1) + lane;
     const int64_t ngroups = (nch + kGroup - 1) / kGroup;
 
+    // Issue priority.  The SIMD issues the oldest ready wave first, so waves
+    // that started later fall behind once compactions compete for issue slots.
+    // A streaming wave takes priority 3..1 as it advances through its piece, so
+    // the ones behind win; a wave that compacts drops to 0, so waves about to
+    // issue loads keep the memory pipe full while it works.
+    auto set_stream_prio = [](int64_t g_done, int64_t g_total) {
+        const int64_t q = g_total > 0 ? (g_done * 3) / g_total : 0;
+        if (q == 0) __builtin_amdgcn_s_setprio(3);
+        else if (q == 1) __builtin_amdgcn_s_setprio(2);
+        else __builtin_amdgcn_s_setprio(1);
+    };
     __builtin_amdgcn_s_setprio(3);
 
     // Head: fewer than kVec elements, the stage is empty.
@@ -348,17 +361,7 @@ void topk_rows_stream_kernel(
                 for (int u = 0; u < kGroup; ++u) A[u] = B[u];
                 load_group(B, gi + 1 < ngroups ? gi + 1 : gi);
                 if constexpr (P > 1) refresh();
-                // The SIMD issues the oldest ready wave first, so waves that started
-                // later fall behind once their compactions compete for issue slots.
-                // A wave lowers its priority as it advances through its piece, so
-                // the ones behind win instead and all finish together.
-                if ((gi & 7) == 0) {
-                    const int64_t q = (gi * 4) / ngroups;
-                    if (q == 0) __builtin_amdgcn_s_setprio(3);
-                    else if (q == 1) __builtin_amdgcn_s_setprio(2);
-                    else if (q == 2) __builtin_amdgcn_s_setprio(1);
-                    else __builtin_amdgcn_s_setprio(0);
-                }
+                if ((gi & 7) == 0) set_stream_prio(gi, ngroups);
             }
         }
         if (!need && phase == 1) {
@@ -377,6 +380,7 @@ void topk_rows_stream_kernel(
         if (!need && phase == 2 && cnt == 0) break;
 
         // Compaction (single call site): L <- exact top-k of L and the stage.
+        __builtin_amdgcn_s_setprio(0);
         wave_lds_sync();
         uint64_t v[E + ES];
 #pragma unroll
@@ -384,7 +388,8 @@ void topk_rows_stream_kernel(
 #pragma unroll
         for (int r = 0; r < ES; ++r) {
             const int idx = r * kWave + lane;
-            v[E + r] = idx < cnt ? stage[idx] : 0ull;
+            const uint64_t raw = idx < cnt ? stage[idx] : 0ull;
+            v[E + r] = idx < cnt ? composite(key32_of_bits((uint32_t)(raw >> 32)), composite_id(raw)) : 0ull;
         }
         const uint64_t T0 = nl + cnt > k ? wave_radix_kth<E + ES>(v, k, hist) : 1ull;
         wave_lds_sync();
@@ -418,6 +423,7 @@ void topk_rows_stream_kernel(
             }
         }
         refresh();
+        set_stream_prio(gi, ngroups);
         if (pend) {
             // The stage is empty now, so the rest of the chunk fits.
 #pragma unroll
