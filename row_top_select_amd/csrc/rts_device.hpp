@@ -147,14 +147,19 @@ __device__ __forceinline__ void bitonic_stage(uint64_t (&v)[N], int lane, int k,
     }
 }
 
-// Full sort: ascending (DESC=false) or descending.
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+// Full sort: ascending (DESC=false) or descending.  Both loops have constant
+// trip counts so that every stage unrolls with constant k and j.
 template <int N, bool DESC>
 __device__ __forceinline__ void wave_bitonic_sort(uint64_t (&v)[N]) {
     const int lane = lane_id();
+    constexpr int LOG = ilog2(kWave * N);
 #pragma unroll
-    for (int k = 2; k <= kWave * N; k <<= 1) {
+    for (int kl = 1; kl <= LOG; ++kl) {
 #pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) bitonic_stage<N, DESC>(v, lane, k, j);
+        for (int jl = LOG - 1; jl >= 0; --jl)
+            if (jl < kl) bitonic_stage<N, DESC>(v, lane, 1 << kl, 1 << jl);
     }
 }
 
@@ -199,6 +204,12 @@ __device__ __forceinline__ uint32_t wave_sum32(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t wave_or32(uint32_t v) {
     return wave_reduce32(v, [](uint32_t a, uint32_t b) { return a | b; });
+}
+__device__ __forceinline__ uint32_t wave_max32(uint32_t v) {
+    return wave_reduce32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min32(uint32_t v) {
+    return wave_reduce32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 __device__ __forceinline__ uint64_t wave_min64(uint64_t v) {
     return wave_reduce64(v, [](uint64_t a, uint64_t b) { return umin64(a, b); });

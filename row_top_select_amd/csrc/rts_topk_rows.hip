@@ -78,93 +78,114 @@ __device__ __forceinline__ void unpack(typename RowTraits<BF16>::vec v, uint32_t
     }
 }
 
-// One level of the wave radix select: bins of [mn, mx] of the composites in
-// [lo_edge, hi_edge] (all nonzero ones on the first level).  Returns true when
-// done, with *T set; otherwise narrows [lo_edge, hi_edge] and need.
-template <int NV, bool FIRST>
-__device__ __forceinline__ bool wave_radix_level(const uint64_t (&v)[NV], uint64_t& lo_edge,
-                                                 uint64_t& hi_edge, int& need, uint64_t* T,
-                                                 uint32_t* hist, bool force_end) {
+// ---------------------------------------------------------------------------
+// Exact k-th composite of a wave-held set (the compaction's select).
+//
+// A window [w, w + span] of one 32-bit word is cut into 256 bins of width
+// 2^s, counted in wave-private LDS.  The bin where the count from the top
+// reaches `need` becomes the next window (s drops by 8), first on the key
+// word, then, when the k-th key is tied, on the low (id) word of the entries
+// with that key.  Bins are sized from the known range, so no level needs a
+// min/max pass, and a register whose entries all lie outside the window
+// costs two compares.
+// ---------------------------------------------------------------------------
+
+// Counts the entries whose word x = word - w lies in [0, span] into bin
+// x >> s.  LO: the word is the low word, and only entries whose key equals
+// key_eq count (a tie level).  Empty entries (0) never count: their key is 0,
+// below every window.
+template <int NV, bool LO>
+__device__ __forceinline__ void radix_hist(const uint64_t (&v)[NV], uint32_t w, uint32_t span,
+                                           uint32_t s, uint32_t key_eq, uint32_t* hist) {
     const int lane = lane_id();
-    uint64_t mn = ~0ull, mx = 0;
-#pragma unroll
-    for (int r = 0; r < NV; ++r) {
-        const bool in = FIRST ? v[r] != 0ull : (v[r] >= lo_edge && v[r] <= hi_edge);
-        mn = in ? umin64(mn, v[r]) : mn;
-        mx = in ? umax64(mx, v[r]) : mx;
-    }
-    mn = wave_min64(mn);
-    mx = wave_max64(mx);
-    if (mn == mx) {
-        *T = mn;
-        return true;
-    }
-    const uint64_t d = mx - mn;
-    const int bl = 64 - __clzll((long long)d);
-    const int s = bl > 8 ? bl - 8 : 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<u32x4_t*>(hist + 4 * lane) = u32x4_t{0u, 0u, 0u, 0u};
     wave_lds_sync();
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
-        const bool in = FIRST ? v[r] != 0ull : (v[r] >= lo_edge && v[r] <= hi_edge);
-        if (in)
-            __hip_atomic_fetch_add(&hist[(uint32_t)((v[r] - mn) >> s)], 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WAVEFRONT);
+        const uint32_t hi = (uint32_t)(v[r] >> 32);
+        const uint32_t x = (LO ? (uint32_t)v[r] : hi) - w;
+        const bool in = LO ? (hi == key_eq && x <= span) : x <= span;
+        if (in) __hip_atomic_fetch_add(&hist[x >> s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
     }
     wave_lds_sync();
-    // Lane l owns bins 255-4l .. 252-4l, scanned from the top.
-    uint32_t c[4];
+}
+
+// Scans the bins from the top: finds the bin where the running count reaches
+// need, lowers need by the count above it and returns the bin and its count
+// (uniform).  False only if the counts were inconsistent.
+__device__ __forceinline__ bool radix_find(const uint32_t* hist, int& need, uint32_t& bin,
+                                           uint32_t& cb) {
+    const int lane = lane_id();
+    uint32_t c[4];  // lane l owns bins 255-4l .. 252-4l
 #pragma unroll
     for (int j = 0; j < 4; ++j) c[j] = hist[255 - 4 * lane - j];
     const uint32_t tot = c[0] + c[1] + c[2] + c[3];
     uint32_t run = wave_incl_scan32(tot) - tot;
     int fj = -1;
-    uint32_t above = 0, cb = 0;
+    uint32_t above = 0, cl = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if (fj < 0 && run < (uint32_t)need && run + c[j] >= (uint32_t)need) {
             fj = j;
             above = run;
-            cb = c[j];
+            cl = c[j];
         }
         run += c[j];
     }
-    wave_lds_sync();
+    wave_lds_sync();  // the next level clears the bins
     const uint64_t fm = __ballot(fj >= 0);
-    if (fm == 0ull || force_end) {  // only if the count invariant were broken
-        *T = mn;
-        return true;
-    }
+    if (fm == 0ull) return false;
     const int fl = __ffsll((long long)fm) - 1;
-    const int bj = __builtin_amdgcn_readlane(fj, fl);
-    above = __builtin_amdgcn_readlane(above, fl);
-    cb = __builtin_amdgcn_readlane(cb, fl);
-    const uint32_t bin = 255u - 4u * (uint32_t)fl - (uint32_t)bj;
-    need -= (int)above;
-    const uint64_t blo = mn + ((uint64_t)bin << s);
-    if ((int)cb == need) {
-        *T = blo;
-        return true;
-    }
-    lo_edge = blo;
-    // The top bin ends at mx (blo + 2^s - 1 could wrap past 2^64 there).
-    hi_edge = bin == (uint32_t)(d >> s) ? mx : blo + ((1ull << s) - 1ull);
-    return false;
+    bin = 255u - 4u * (uint32_t)fl - (uint32_t)__builtin_amdgcn_readlane(fj, fl);
+    need -= (int)__builtin_amdgcn_readlane(above, fl);
+    cb = __builtin_amdgcn_readlane(cl, fl);
+    return true;
 }
 
-// Exact k-th largest composite among v[] (0 = empty); requires k <= number of
-// nonzero entries.  Returns T such that exactly k nonzero entries are >= T
-// when composites are distinct.  hist: 256 wave-private LDS counters.  Each
-// level narrows the range by at least 2^7, so 10 levels always finish; the
-// cap only bounds the loop if the count invariant were ever broken.
+// T such that exactly `need` nonzero entries of v[] are >= T (composites are
+// distinct).  Requires at least `need` nonzero entries, all with key >= lb.
 template <int NV>
-__device__ __forceinline__ uint64_t wave_radix_kth(const uint64_t (&v)[NV], int k, uint32_t* hist) {
-    uint64_t lo_edge = 1, hi_edge = ~0ull, T = 0;
-    int need = k;
-    if (wave_radix_level<NV, true>(v, lo_edge, hi_edge, need, &T, hist, false)) return T;
-    for (int level = 1;; ++level)
-        if (wave_radix_level<NV, false>(v, lo_edge, hi_edge, need, &T, hist, level >= 12)) return T;
+__device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[NV], int need, uint32_t lb,
+                                             uint32_t* hist) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int r = 0; r < NV; ++r) mx = mx > (uint32_t)(v[r] >> 32) ? mx : (uint32_t)(v[r] >> 32);
+    mx = wave_max32(mx);
+    // Key levels: s starts at most at 24 and drops by 8, so the fourth level
+    // has s == 0 (bins of one key).
+    uint32_t w = lb, span = mx - lb;
+    const int bl = span ? 32 - __clz((int)span) : 0;
+    uint32_t s = bl > 8 ? (uint32_t)(bl - 8) : 0u;
+#pragma unroll 1
+    for (int level = 0; level < 4; ++level) {
+        radix_hist<NV, false>(v, w, span, s, 0u, hist);
+        uint32_t bin, cb;
+        if (!radix_find(hist, need, bin, cb)) return (uint64_t)w << 32;
+        const uint32_t blo = w + (bin << s);
+        if ((int)cb == need) return (uint64_t)blo << 32;
+        w = blo;
+        if (s == 0) break;  // the k-th key is tied
+        // Entries never exceed mx, so the window stays below 2^32.
+        const uint32_t top = mx - blo, width = (1u << s) - 1u;
+        span = width < top ? width : top;
+        s = s > 8 ? s - 8 : 0u;
+    }
+    // Tie levels on the low word among the entries with key w.
+    const uint32_t key = w;
+    uint32_t wl = 0, spl = 0xFFFFFFFFu, sl = 24;
+#pragma unroll 1
+    for (int level = 0; level < 4; ++level) {
+        radix_hist<NV, true>(v, wl, spl, sl, key, hist);
+        uint32_t bin, cb;
+        if (!radix_find(hist, need, bin, cb)) break;
+        const uint32_t blo = wl + (bin << sl);
+        if ((int)cb == need || sl == 0) return ((uint64_t)key << 32) | blo;
+        spl = (1u << sl) - 1u;
+        wl = blo;
+        sl -= 8;
+    }
+    return ((uint64_t)key << 32) | wl;
 }
 
 template <int E, int ES, bool BF16, int P>
@@ -199,13 +220,13 @@ void topk_rows_stream_kernel(
         __syncthreads();
     }
 
-    // This wave's piece [a, b) of the row.
+    // This wave's piece [a, b) of the row (columns fit in 31 bits).
     const int64_t pieces = (int64_t)groups * P;
     const int64_t piece = (int64_t)g * P + wave;
     int64_t per = (e + pieces - 1) / pieces;
     per = (per + kChunk - 1) / kChunk * kChunk;
-    const int64_t a = piece * per < e ? piece * per : e;
-    const int64_t b = a + per < e ? a + per : e;
+    const int a = (int)(piece * per < e ? piece * per : e);
+    const int b = (int)(a + per < e ? a + per : e);
 
     const T* rowp = reinterpret_cast<const T*>(xv) + row * ld;
 
@@ -213,7 +234,7 @@ void topk_rows_stream_kernel(
     int nl = 0;                      // entries in the register list L (wave-uniform)
     uint32_t thr_own = 0x007FFFFFu;  // key of -inf: every non-NaN value passes
     float f = float_of_key32(thr_own);
-    // The current top list: up to k composites, E per lane, unsorted.
+    // The current top list: up to k composites, E per lane, in no order.
     uint64_t L[E];
 #pragma unroll
     for (int r = 0; r < E; ++r) L[r] = 0;
@@ -228,140 +249,181 @@ void topk_rows_stream_kernel(
         f = float_of_key32(t);
     };
 
-    // Staged entries hold the raw score bits in the high word (the key transform
-    // is applied once per entry when the stage is compacted).
-    auto append = [&](uint64_t m, uint32_t bits, uint32_t col) {
-        if ((m >> lane) & 1ull) stage[cnt + (int)mbcnt64(m)] = composite(bits, col);
-        cnt += (int)__popcll(m);
+    // Staged entries hold the raw score bits in the high word and 2^32-1-col
+    // in the low word; the key transform is applied when the stage is
+    // compacted.
+    auto put = [&](int slot, uint32_t bits, uint32_t idn) {
+        uint32_t* p = reinterpret_cast<uint32_t*>(stage + slot);
+        p[0] = idn;
+        p[1] = bits;
     };
 
     // Elements one per lane (head and tail of the piece); needs 64 free slots.
     auto consider = [&](uint32_t bits, uint32_t col, bool valid) {
-        const uint64_t m = __ballot(valid && __uint_as_float(bits) >= f);
-        if (m) append(m, bits, col);
+        const bool pass = valid && __uint_as_float(bits) >= f;
+        const uint64_t m = __ballot(pass);
+        if (m) {
+            if (pass) put(cnt + (int)mbcnt64(m), bits, 0xFFFFFFFFu - col);
+            cnt += (int)__popcll(m);
+        }
     };
 
     // Geometry: head [a, a1) up to the first aligned vector, body of whole
     // chunks, tail [t0, b).
-    int64_t a1 = a, nch = 0, t0 = a;
+    int a1 = a, nch = 0, t0 = a;
     if (a < b) {
-        constexpr int64_t vbytes = sizeof(V);
+        constexpr int vbytes = sizeof(V);
         const uintptr_t base = reinterpret_cast<uintptr_t>(rowp);
-        const int64_t off = (int64_t)((base % vbytes) / sizeof(T));
+        const int off = (int)((base % vbytes) / sizeof(T));
         a1 = a + (kVec - (off + a) % kVec) % kVec;
         a1 = a1 < b ? a1 : b;
         nch = (b - a1) / kChunk;
         t0 = a1 + nch * kChunk;
     }
-    const V* bp = reinterpret_cast<const V*>(rowp + a1) + lane;
-    const int64_t ngroups = (nch + kGroup - 1) / kGroup;
+    const V* cbase = reinterpret_cast<const V*>(rowp + a1);  // wave-uniform
+    const int ngroups = (nch + kGroup - 1) / kGroup;
+    // 2^32-1 minus this lane's first column in chunk 0.
+    const uint32_t idn0 = 0xFFFFFFFFu - (uint32_t)(a1 + lane * kVec);
 
     // Issue priority.  The SIMD issues the oldest ready wave first, so waves
     // that started later fall behind once compactions compete for issue slots.
     // A streaming wave takes priority 3..1 as it advances through its piece, so
     // the ones behind win; a wave that compacts drops to 0, so waves about to
     // issue loads keep the memory pipe full while it works.
-    auto set_stream_prio = [](int64_t g_done, int64_t g_total) {
-        const int64_t q = g_total > 0 ? (g_done * 3) / g_total : 0;
-        if (q == 0) __builtin_amdgcn_s_setprio(3);
-        else if (q == 1) __builtin_amdgcn_s_setprio(2);
+    const int g1 = ngroups / 3, g2 = (2 * ngroups) / 3;
+    auto set_stream_prio = [&](int gdone) {
+        if (gdone < g1) __builtin_amdgcn_s_setprio(3);
+        else if (gdone < g2) __builtin_amdgcn_s_setprio(2);
         else __builtin_amdgcn_s_setprio(1);
     };
     __builtin_amdgcn_s_setprio(3);
 
     // Head: fewer than kVec elements, the stage is empty.
     if (a1 > a) {
-        const int64_t col = a + lane;
+        const int col = a + lane;
         const bool valid = col < a1;
         consider(valid ? load_bits<BF16>(rowp + col) : 0u, (uint32_t)col, valid);
     }
 
     V A[kGroup], B[kGroup];
-    auto load_group = [&](V(&dst)[kGroup], int64_t gi) {
+    // Loads group gi; past the last group every load re-reads the last chunk
+    // (just read by this wave, an L2 hit), so the refills are unconditional
+    // and the order of outstanding loads is the same on every path.
+    auto load_group = [&](V(&dst)[kGroup], int gi) {
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
-            int64_t c = gi * kGroup + u;
-            c = c < nch ? c : nch - 1;
-            dst[u] = __builtin_nontemporal_load(bp + c * kWave);
+            uint32_t c = (uint32_t)(gi * kGroup + u);
+            c = c < (uint32_t)nch ? c : (uint32_t)nch - 1u;
+            const V* gp = cbase + (uint64_t)c * kWave;  // wave-uniform
+            dst[u] = __builtin_nontemporal_load(gp + lane);
         }
     };
-    int64_t gi = 0;
+    int gi = 0;
     if (ngroups > 0) {
         load_group(A, 0);
-        load_group(B, ngroups > 1 ? 1 : 0);
+        load_group(B, 1);
     }
-    int ustart = 0;  // first chunk of the group still to process
-    // A chunk interrupted by a full stage: its masks (taken against the older,
-    // lower threshold: a superset) and values; finished right after the
-    // compaction.  Re-filtering it strictly could drop a tie whose id is smaller
-    // than that of an entry of the same chunk already in the list.
-    bool pend = false;
-    int pend_c = 0;
-    uint32_t pbits[kVec] = {0, 0, 0, 0};
-    uint64_t pm[kVec] = {0, 0, 0, 0};
-    uint32_t pcol0 = 0;
-    int64_t tpos = t0;
+    // First chunk of group A still to filter.  A chunk whose survivors do not
+    // fit in the stage is left whole and filtered again after the compaction
+    // (against the raised threshold: its elements come after every listed
+    // one, so a tie with the k-th listed key loses and the strict filter is
+    // exact).
+    int ustart = 0;
+    int tpos = t0;
     int phase = ngroups > 0 ? 0 : 1;  // 0 body, 1 tail, 2 end
 
-    // One chunk: returns false (after saving the rest as pending) if the stage
-    // filled up inside it.
-    auto chunk = [&](V vv, uint32_t col0, int u) -> bool {
+    // One chunk (lane l holds columns col0+4l .. col0+4l+3, idn = 2^32-1 -
+    // (col0+4l)): stages every survivor, or nothing and returns false when
+    // they do not all fit.
+    auto chunk = [&](V vv, uint32_t idn) -> bool {
         uint32_t bits[kVec];
         unpack<BF16>(vv, bits);
+        bool pass[kVec];
         uint64_t m[kVec];
 #pragma unroll
-        for (int c = 0; c < kVec; ++c) m[c] = __ballot(__uint_as_float(bits[c]) >= f);
+        for (int c = 0; c < kVec; ++c) {
+            pass[c] = __uint_as_float(bits[c]) >= f;
+            m[c] = __ballot(pass[c]);
+        }
         if ((m[0] | m[1] | m[2] | m[3]) == 0ull) return true;
+        int n[kVec];
+#pragma unroll
+        for (int c = 0; c < kVec; ++c) n[c] = (int)__popcll(m[c]);
+        if (cnt + n[0] + n[1] + n[2] + n[3] > SCAP) return false;
 #pragma unroll
         for (int c = 0; c < kVec; ++c) {
             if (m[c]) {
-                if (cnt + kWave > SCAP) {
-                    pend = true;
-                    pend_c = c;
-                    pcol0 = col0;
-#pragma unroll
-                    for (int q = 0; q < kVec; ++q) {
-                        pbits[q] = bits[q];
-                        pm[q] = m[q];
-                    }
-                    ustart = u + 1;
-                    return false;
-                }
-                append(m[c], bits[c], col0 + (uint32_t)c);
+                if (pass[c]) put(cnt + (int)mbcnt64(m[c]), bits[c], idn - (uint32_t)c);
+                cnt += n[c];
             }
         }
         return true;
     };
 
+    // Filters the chunks ustart.. of group gi held in buf; true if the stage
+    // filled up (ustart then names the chunk to filter again).
+    auto run_group = [&](V(&buf)[kGroup]) -> bool {
+        const uint32_t idg = idn0 - (uint32_t)(gi * kGroup * kChunk);
+        if (ustart == 0 && (gi + 1) * kGroup <= nch) {
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                if (!chunk(buf[u], idg - (uint32_t)(u * kChunk))) {
+                    ustart = u;
+                    return true;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                if (u >= ustart && gi * kGroup + u < nch &&
+                    !chunk(buf[u], idg - (uint32_t)(u * kChunk))) {
+                    ustart = u;
+                    return true;
+                }
+            }
+        }
+        return false;
+    };
+    // The buffers alternate: A holds group gi and B group gi + 1 at the top of
+    // an iteration; each is refilled with the group after next as soon as it
+    // is consumed, so two groups stay in flight without register copies.  The
+    // body is straight-line (A half, then B half), so at the back edge B's
+    // loads are always the younger ones.  half == 1 only on re-entry after a
+    // compaction that interrupted the B half.
+    int half = 0;
+
     for (;;) {
         bool need = false;
         if (phase == 0) {
             while (true) {
-                if (ustart == 0 && (gi + 1) * kGroup <= nch) {
-#pragma unroll
-                    for (int u = 0; u < kGroup; ++u) {
-                        if (!need)
-                            need = !chunk(A[u], (uint32_t)(a1 + (gi * kGroup + u) * kChunk + lane * kVec), u);
+                if (half == 0) {
+                    if (run_group(A)) {
+                        need = true;
+                        break;
                     }
-                } else {
-#pragma unroll
-                    for (int u = 0; u < kGroup; ++u) {
-                        if (!need && u >= ustart && gi * kGroup + u < nch)
-                            need = !chunk(A[u], (uint32_t)(a1 + (gi * kGroup + u) * kChunk + lane * kVec), u);
+                    load_group(A, gi + 2);
+                    ustart = 0;
+                    if (++gi >= ngroups) {
+                        phase = 1;
+                        break;
                     }
+                    if constexpr (P > 1) refresh();
+                    if ((gi & 7) == 0) set_stream_prio(gi);
                 }
-                if (need) break;
+                half = 0;
+                if (run_group(B)) {
+                    half = 1;
+                    need = true;
+                    break;
+                }
+                load_group(B, gi + 2);
                 ustart = 0;
-                ++gi;
-                if (gi >= ngroups) {
+                if (++gi >= ngroups) {
                     phase = 1;
                     break;
                 }
-#pragma unroll
-                for (int u = 0; u < kGroup; ++u) A[u] = B[u];
-                load_group(B, gi + 1 < ngroups ? gi + 1 : gi);
                 if constexpr (P > 1) refresh();
-                if ((gi & 7) == 0) set_stream_prio(gi, ngroups);
+                if ((gi & 7) == 0) set_stream_prio(gi);
             }
         }
         if (!need && phase == 1) {
@@ -370,7 +432,7 @@ void topk_rows_stream_kernel(
                     need = true;
                     break;
                 }
-                const int64_t col = tpos + lane;
+                const int col = tpos + lane;
                 const bool valid = col < b;
                 consider(valid ? load_bits<BF16>(rowp + col) : 0u, (uint32_t)col, valid);
                 tpos += kWave;
@@ -389,51 +451,57 @@ void topk_rows_stream_kernel(
         for (int r = 0; r < ES; ++r) {
             const int idx = r * kWave + lane;
             const uint64_t raw = idx < cnt ? stage[idx] : 0ull;
-            v[E + r] = idx < cnt ? composite(key32_of_bits((uint32_t)(raw >> 32)), composite_id(raw)) : 0ull;
+            v[E + r] = idx < cnt ? ((uint64_t)key32_of_bits((uint32_t)(raw >> 32)) << 32) |
+                                       (uint32_t)raw
+                                 : 0ull;
         }
-        const uint64_t T0 = nl + cnt > k ? wave_radix_kth<E + ES>(v, k, hist) : 1ull;
-        wave_lds_sync();
+        // Every entry has key >= thr_own - 1: the list's entries are at or
+        // above its k-th key, and the filter passes keys >= thr_own (-0 also
+        // passes a +0 threshold, one key below).
+        const uint64_t T0 = nl + cnt > k ? wave_kth<E + ES>(v, k, thr_own - 1u, hist) : 1ull;
         int base = 0;
-        uint64_t kth = ~0ull;
+        uint32_t kmin = 0xFFFFFFFFu;
 #pragma unroll
         for (int r = 0; r < E + ES; ++r) {
-            const bool sel = v[r] != 0ull && v[r] >= T0;
+            const bool sel = v[r] >= T0;  // T0 >= 1: empty slots never
             const uint64_t m = __ballot(sel);
-            if (sel) stage[base + (int)mbcnt64(m)] = v[r];
-            base += (int)__popcll(m);
-            kth = sel ? umin64(kth, v[r]) : kth;
+            const int nsel = (int)__popcll(m);
+            // Exactly k entries are selected; the bound only guards the
+            // stage if that were ever not so.
+            if (sel && base + nsel <= SBUF) {
+                stage[base + (int)mbcnt64(m)] = v[r];
+                const uint32_t key = (uint32_t)(v[r] >> 32);
+                kmin = key < kmin ? key : kmin;
+            }
+            base += base + nsel <= SBUF ? nsel : 0;
         }
         // Distinct composites leave at most k; never exceed the list.
         nl = base < LP ? base : LP;
         wave_lds_sync();
 #pragma unroll
         for (int r = 0; r < E; ++r) {
-            const int idx = lane * E + r;
+            const int idx = r * kWave + lane;
             L[r] = idx < nl ? stage[idx] : 0ull;
         }
         wave_lds_sync();
         cnt = 0;
         if (nl >= k) {
-            kth = wave_min64(kth);
-            thr_own = (uint32_t)(kth >> 32) + 1u;
+            const uint32_t kth = wave_min32(kmin);
+            thr_own = kth + 1u;
             if constexpr (P > 1) {
                 if (lane == 0)
-                    __hip_atomic_fetch_max(&thr_shared, (uint32_t)(kth >> 32), __ATOMIC_RELAXED,
+                    __hip_atomic_fetch_max(&thr_shared, kth, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
         refresh();
-        set_stream_prio(gi, ngroups);
-        if (pend) {
-            // The stage is empty now, so the rest of the chunk fits.
-#pragma unroll
-            for (int c = 0; c < kVec; ++c)
-                if (c >= pend_c && pm[c]) append(pm[c], pbits[c], pcol0 + (uint32_t)c);
-            pend = false;
-        }
-        if (phase == 2 && cnt == 0) break;
+        set_stream_prio(gi);
+        if (phase == 2) break;
+        // Every load has landed by now (the compaction is long); waiting here
+        // keeps the compiler's view of which buffer is younger exact at the
+        // loop head, so the stream loop waits only for the buffer it reads.
+        __builtin_amdgcn_s_waitcnt(0);
     }
-
     // The wave's top list, sorted descending, blocked (lane l: l*E .. l*E+E-1).
     wave_bitonic_sort<E, true>(L);
 
