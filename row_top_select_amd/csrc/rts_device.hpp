@@ -104,6 +104,14 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Lane-wise select by a wave mask: if_set where the lane's bit of m is set.
+// One v_cndmask; written out so the compiler cannot turn it into a branch.
+__device__ __forceinline__ uint32_t select_by_mask(uint64_t m, uint32_t if_set, uint32_t if_clear) {
+    uint32_t r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if_clear), "v"(if_set), "s"(m));
+    return r;
+}
+
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a < b ? b : a; }
 

@@ -201,8 +201,9 @@ void topk_rows_stream_kernel(
     constexpr int SBUF = SCAP > LP ? SCAP : LP;  // also carries the selected list into L
     static_assert(SCAP >= kChunk, "the stage must take a whole chunk");
 
-    __shared__ uint64_t stage_all[P][SBUF];
-    __shared__ uint32_t hist_all[P][256];
+    // SBUF slots, then one slot per lane where lanes that fail the filter write.
+    __shared__ uint64_t stage_all[P][SBUF + kWave];
+    __shared__ __attribute__((aligned(16))) uint32_t hist_all[P][256];
     __shared__ uint32_t thr_shared;
 
     const int lane = lane_id();
@@ -334,7 +335,8 @@ void topk_rows_stream_kernel(
 
     // One chunk (lane l holds columns col0+4l .. col0+4l+3, idn = 2^32-1 -
     // (col0+4l)): stages every survivor, or nothing and returns false when
-    // they do not all fit.
+    // they do not all fit.  Lanes whose element fails write their own sink
+    // slot past the stage instead, so a component costs no exec-mask changes.
     auto chunk = [&](V vv, uint32_t idn) -> bool {
         uint32_t bits[kVec];
         unpack<BF16>(vv, bits);
@@ -346,15 +348,17 @@ void topk_rows_stream_kernel(
             m[c] = __ballot(pass[c]);
         }
         if ((m[0] | m[1] | m[2] | m[3]) == 0ull) return true;
-        int n[kVec];
-#pragma unroll
-        for (int c = 0; c < kVec; ++c) n[c] = (int)__popcll(m[c]);
-        if (cnt + n[0] + n[1] + n[2] + n[3] > SCAP) return false;
+        // A chunk adds at most kChunk entries: count exactly only near full.
+        if (cnt > SCAP - kChunk &&
+            cnt + (int)(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3])) > SCAP)
+            return false;
 #pragma unroll
         for (int c = 0; c < kVec; ++c) {
             if (m[c]) {
-                if (pass[c]) put(cnt + (int)mbcnt64(m[c]), bits[c], idn - (uint32_t)c);
-                cnt += n[c];
+                const int slot = (int)select_by_mask(m[c], (uint32_t)cnt + mbcnt64(m[c]),
+                                                     (uint32_t)(SBUF + lane));
+                stage[slot] = ((uint64_t)bits[c] << 32) | (idn - (uint32_t)c);
+                cnt += (int)__popcll(m[c]);
             }
         }
         return true;
