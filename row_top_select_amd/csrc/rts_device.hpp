@@ -81,11 +81,8 @@ __device__ __forceinline__ uint32_t lane_xor32(uint32_t v, int lj) {
     switch (lj) {
         case 1: return dpp32<kDppQuadXor1>(v, v);
         case 2: return dpp32<kDppQuadXor2>(v, v);
-        case 4: {
-            const uint32_t up = dpp32<kDppRowShl4>(v, v);
-            const uint32_t dn = dpp32<kDppRowShr4>(v, v);
-            return (__lane_id() & 4) ? dn : up;
-        }
+        // ds_swizzle bit mode: lane' = ((lane & 0x1F) | 0) ^ xor within 32 lanes.
+        case 4: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);
         case 8: return dpp32<kDppRowRor8>(v, v);
         case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
         default: return (uint32_t)__shfl_xor((int)v, lj, kWave);
@@ -126,58 +123,90 @@ __device__ __forceinline__ void wave_lds_sync() {
 // ---------------------------------------------------------------------------
 // Bitonic network over 64*N values held "blocked" by one wave: lane l holds
 // elements l*N .. l*N+N-1 in v[0..N-1].  Partners closer than N are in the
-// same lane; farther partners are exchanged with a lane xor.
+// same lane; farther partners are exchanged with a lane xor.  Which lanes sort
+// a pair descending, or keep the larger partner, is a fixed pattern of lane
+// bits per stage, so a compare-exchange is one 64-bit compare, one scalar xor
+// of wave masks and a select per word.
 // ---------------------------------------------------------------------------
-template <int N, bool DESC>
-__device__ __forceinline__ void bitonic_stage(uint64_t (&v)[N], int lane, int k, int j) {
-    if (j < N) {
+
+// Lanes whose index has bit x set (x a power of two); none for x >= 64.
+__device__ __forceinline__ constexpr uint64_t lanes_with_bit(int x) {
+    return x == 1    ? 0xAAAAAAAAAAAAAAAAull
+           : x == 2  ? 0xCCCCCCCCCCCCCCCCull
+           : x == 4  ? 0xF0F0F0F0F0F0F0F0ull
+           : x == 8  ? 0xFF00FF00FF00FF00ull
+           : x == 16 ? 0xFFFF0000FFFF0000ull
+           : x == 32 ? 0xFFFFFFFF00000000ull
+                     : 0ull;
+}
+
+__device__ __forceinline__ uint64_t select64_by_mask(uint64_t m, uint64_t if_set, uint64_t if_clear) {
+    const uint32_t lo = select_by_mask(m, (uint32_t)if_set, (uint32_t)if_clear);
+    const uint32_t hi = select_by_mask(m, (uint32_t)(if_set >> 32), (uint32_t)(if_clear >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int N, bool DESC, int K, int J>
+__device__ __forceinline__ void bitonic_stage(uint64_t (&v)[N]) {
+    // Element i = l*N + r lies in an ascending run iff (i & K) == 0 (the
+    // reverse for DESC).  For K >= N that is bit K/N of the lane.
+    constexpr uint64_t flip = DESC ? ~0ull : 0ull;
+    if constexpr (J < N) {
 #pragma unroll
         for (int r = 0; r < N; ++r) {
-            if ((r & j) == 0) {
-                const int i = lane * N + r;
-                const bool up = ((i & k) == 0) != DESC;
-                const uint64_t a = v[r], b = v[r | j];
-                const bool sw = up ? (a > b) : (a < b);
-                v[r] = sw ? b : a;
-                v[r | j] = sw ? a : b;
+            if ((r & J) == 0) {
+                const uint64_t desc =
+                    (K < N ? (((r & K) != 0) ? ~0ull : 0ull) : lanes_with_bit(K / N)) ^ flip;
+                const uint64_t a = v[r], b = v[r | J];
+                // Ascending: swap if a > b; descending: if a < b (equal: either).
+                const uint64_t sw = __ballot(a > b) ^ desc;
+                v[r] = select64_by_mask(sw, b, a);
+                v[r | J] = select64_by_mask(sw, a, b);
             }
         }
     } else {
-        const int lj = j / N;
-        const bool lower = (lane & lj) == 0;
+        constexpr int LJ = J / N;
+        constexpr uint64_t desc = lanes_with_bit(K / N) ^ flip;
+        // The lower partner keeps the smaller value in an ascending run.
+        constexpr uint64_t keep_max = lanes_with_bit(LJ) ^ desc;
 #pragma unroll
         for (int r = 0; r < N; ++r) {
-            const uint64_t o = shfl_xor64(v[r], lj);
-            const int i = lane * N + r;
-            const bool up = ((i & k) == 0) != DESC;
-            v[r] = (lower == up) ? umin64(v[r], o) : umax64(v[r], o);
+            const uint64_t o = shfl_xor64(v[r], LJ);
+            const uint64_t take = __ballot(v[r] > o) ^ keep_max;
+            v[r] = select64_by_mask(take, o, v[r]);
         }
     }
 }
 
-constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+// Stages J, J/2, .., 1 of the merge step of size K.
+template <int N, bool DESC, int K, int J>
+__device__ __forceinline__ void bitonic_steps(uint64_t (&v)[N]) {
+    if constexpr (J >= 1) {
+        bitonic_stage<N, DESC, K, J>(v);
+        bitonic_steps<N, DESC, K, J / 2>(v);
+    }
+}
 
-// Full sort: ascending (DESC=false) or descending.  Both loops have constant
-// trip counts so that every stage unrolls with constant k and j.
+template <int N, bool DESC, int K>
+__device__ __forceinline__ void bitonic_sort_from(uint64_t (&v)[N]) {
+    if constexpr (K <= kWave * N) {
+        bitonic_steps<N, DESC, K, K / 2>(v);
+        bitonic_sort_from<N, DESC, K * 2>(v);
+    }
+}
+
+// Full sort: ascending (DESC=false) or descending.  Every stage is its own
+// instantiation, so k and j are constants without relying on loop unrolling.
 template <int N, bool DESC>
 __device__ __forceinline__ void wave_bitonic_sort(uint64_t (&v)[N]) {
-    const int lane = lane_id();
-    constexpr int LOG = ilog2(kWave * N);
-#pragma unroll
-    for (int kl = 1; kl <= LOG; ++kl) {
-#pragma unroll
-        for (int jl = LOG - 1; jl >= 0; --jl)
-            if (jl < kl) bitonic_stage<N, DESC>(v, lane, 1 << kl, 1 << jl);
-    }
+    bitonic_sort_from<N, DESC, 2>(v);
 }
 
 // Sorts a bitonic sequence (e.g. the elementwise max of a descending and an
 // ascending sorted sequence).
 template <int N, bool DESC>
 __device__ __forceinline__ void wave_bitonic_merge(uint64_t (&v)[N]) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int j = (kWave * N) >> 1; j > 0; j >>= 1) bitonic_stage<N, DESC>(v, lane, kWave * N, j);
+    bitonic_steps<N, DESC, kWave * N, kWave * N / 2>(v);
 }
 
 // ---------------------------------------------------------------------------
