@@ -109,6 +109,18 @@ __device__ __forceinline__ uint32_t select_by_mask(uint64_t m, uint32_t if_set, 
     return r;
 }
 
+// LDS byte address of a pointer into __shared__ memory, and a two-word store
+// at such an address (the words come from any two registers).
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_store2(uint32_t addr, uint32_t lo, uint32_t hi) {
+    lds_u32* q = (lds_u32*)(uintptr_t)addr;
+    q[0] = lo;
+    q[1] = hi;
+}
+
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a < b ? b : a; }
 

@@ -337,6 +337,11 @@ void topk_rows_stream_kernel(
     // (col0+4l)): stages every survivor, or nothing and returns false when
     // they do not all fit.  Lanes whose element fails write their own sink
     // slot past the stage instead, so a component costs no exec-mask changes.
+    // Slots are addressed by LDS byte address (a wave-uniform running base
+    // plus 8 * the lane's rank among the component's survivors), and the two
+    // words of an entry are written from their own registers.
+    const uint32_t stage_base = lds_addr(stage);
+    const uint32_t sink = stage_base + (uint32_t)(SBUF + lane) * 8u;
     auto chunk = [&](V vv, uint32_t idn) -> bool {
         uint32_t bits[kVec];
         unpack<BF16>(vv, bits);
@@ -352,15 +357,17 @@ void topk_rows_stream_kernel(
         if (cnt > SCAP - kChunk &&
             cnt + (int)(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3])) > SCAP)
             return false;
+        uint32_t sa = stage_base + (uint32_t)cnt * 8u;
+        asm volatile("" : "+s"(sa));  // keep the base whole: one v_lshl_add per slot
 #pragma unroll
         for (int c = 0; c < kVec; ++c) {
             if (m[c]) {
-                const int slot = (int)select_by_mask(m[c], (uint32_t)cnt + mbcnt64(m[c]),
-                                                     (uint32_t)(SBUF + lane));
-                stage[slot] = ((uint64_t)bits[c] << 32) | (idn - (uint32_t)c);
-                cnt += (int)__popcll(m[c]);
+                const uint32_t a = select_by_mask(m[c], sa + mbcnt64(m[c]) * 8u, sink);
+                lds_store2(a, idn - (uint32_t)c, bits[c]);
+                sa += (uint32_t)__popcll(m[c]) * 8u;
             }
         }
+        cnt = (int)((sa - stage_base) >> 3);
         return true;
     };
 
