@@ -66,13 +66,15 @@ def cpu_baseline(x_sample, ends_sample, k, total_rows_note):
     t0 = time.perf_counter()
     ids = oracle.topk_rows(x_sample, ends_sample, k)
     dt = time.perf_counter() - t0
+    n = x_sample.shape[0]
+    what = (f"all {n} rows" if n == total_rows_note else
+            f"{n} of {total_rows_note} rows (rows 0..{n - 1})")
     return ids, {
-        "value": x_sample.shape[0] / dt,
+        "value": n / dt,
         "unit": "rows/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": f"{x_sample.shape[0]} of {total_rows_note} rows (rows 0..{x_sample.shape[0] - 1}, "
-                  f"same data and row ends), one run, {dt:.2f} s wall",
+        "sample": f"{what} of the same workload (same data and row ends), one run, {dt:.2f} s wall",
     }
 
 
@@ -214,10 +216,10 @@ def main():
                      "algorithmic_bytes": abytes},
     }
     if not args.no_cpu:
-        sample = 1024
-        ids, cpu = cpu_baseline(x_np[:sample], ends_np[:sample], w.k, w.rows)
+        # The whole workload is a few seconds of oracle time on the host's cores.
+        ids, cpu = cpu_baseline(x_np, ends_np, w.k, w.rows)
         result["cpu_baseline"] = cpu
-        result["parity_sample_rows_equal"] = bool(np.array_equal(out[:sample].cpu().numpy(), ids))
+        result["parity_rows_equal"] = bool(np.array_equal(out.cpu().numpy(), ids))
     if args.all:
         del x
         torch.cuda.empty_cache()
