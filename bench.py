@@ -7,8 +7,9 @@ whole matrix, inputs resident in HBM.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--all] [--copy-calib]
 
---all adds the other workloads (prefill, ties, long, decode, packed and pair
-merges) as a "secondary" object; --copy-calib only runs a plain 1 GiB device
+--all adds the other workloads (prefill, ties, long, decode, the 8K x 8K
+distribution ablation, the headline shape in bf16, packed and pair merges) as a
+"secondary" object; --copy-calib only runs a plain 1 GiB device
 copy (the reference point for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling).
 """
 
@@ -81,20 +82,30 @@ def cpu_baseline(x_sample, ends_sample, k, total_rows_note):
 def secondary(torch, rts, datagen, steps, warmup):
     import numpy as np
     res = {}
-    for name in ("prefill", "ties", "long", "decode"):
-        w = datagen.WORKLOADS[name]
-        x = torch.from_numpy(datagen.logits(w)).cuda()
+    # The measured configs, the pages' distribution ablation (8K x 8K: normal,
+    # +100, *1e-8) and the headline shape in bf16.
+    for name in ("prefill", "ties", "long", "decode", "robust", "robust_plus100",
+                 "robust_scale1e8", "verylong_bf16"):
+        bf16 = name.endswith("_bf16")
+        w = datagen.WORKLOADS[name[:-5] if bf16 else name]
+        x_np = datagen.logits(w, threads=8)
+        if bf16:
+            x = torch.from_numpy(datagen.bf16_bits(x_np).view(np.int16)).cuda().view(torch.bfloat16)
+        else:
+            x = torch.from_numpy(x_np).cuda()
+        del x_np
         ends_np = datagen.row_ends(w)
         ends = torch.from_numpy(ends_np).cuda()
         out = torch.empty((w.rows, w.k), dtype=torch.int32, device="cuda")
-        ws_n = rts.topk_rows_workspace_size(torch.float32, w.rows, w.cols, w.k)
+        ws_n = rts.topk_rows_workspace_size(x.dtype, w.rows, w.cols, w.k)
         ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
         _, t = time_calls(lambda: rts.topk_rows(x, w.k, row_ends=ends, out=out,
                                                 workspace=ws if ws_n else None),
                           steps, warmup, torch)
-        b = algorithmic_bytes(ends_np, w.k, w.rows)
-        res[name] = {"shape": [w.rows, w.cols], "k": w.k, "us_per_call": t * 1e6,
-                     "rows_per_s": w.rows / t, "algorithmic_GBps": b / t / 1e9}
+        b = algorithmic_bytes(ends_np, w.k, w.rows, elem=2 if bf16 else 4)
+        res[name] = {"shape": [w.rows, w.cols], "k": w.k, "dtype": "bf16" if bf16 else "f32",
+                     "us_per_call": t * 1e6, "rows_per_s": w.rows / t,
+                     "algorithmic_GBps": b / t / 1e9}
         del x
     # Packed merge (config of 8 simulated ranks) and the pair merge.
     W, R, S, N, K = (datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_LOCAL_COLS,

@@ -21,7 +21,16 @@ verylong   105   4096 x 102400, N(0,1)         98305 + i           512
 decode     106   64 x 102400, N(0,1)           all 102400          512
 merge      107   global 6710 x 131072 N(0,1);  none                2048
                  rank r owns columns g % 8 == r
+robust     108   8192 x 8192, N(0,1)           i + 1               512
+robust_    108   the same values + 100         i + 1               512
+ plus100
+robust_    108   the same values * 1e-8        i + 1               512
+ scale1e8
 =========  ====  ============================  ==================  ====
+
+The three ``robust`` workloads are the pages' distribution ablation at 8K
+queries x 8K keys (one base matrix, shifted or scaled in fp32).  The headline
+shape in bf16 is ``verylong`` rounded with ``bf16_bits``.
 """
 
 from __future__ import annotations
@@ -45,7 +54,7 @@ class Workload:
     rows: int
     cols: int
     k: int
-    kind: str          # "normal", "ties", "specials"
+    kind: str          # "normal", "ties", "specials", "plus100", "scale1e8"
     causal: bool       # row_end[i] = cols - rows + i + 1, else full rows
 
 
@@ -56,6 +65,9 @@ WORKLOADS = {
     "long": Workload("long", 104, 2048, 51200, 512, "specials", True),
     "verylong": Workload("verylong", 105, 4096, 102400, 512, "normal", True),
     "decode": Workload("decode", 106, 64, 102400, 512, "normal", False),
+    "robust": Workload("robust", 108, 8192, 8192, 512, "normal", True),
+    "robust_plus100": Workload("robust_plus100", 108, 8192, 8192, 512, "plus100", True),
+    "robust_scale1e8": Workload("robust_scale1e8", 108, 8192, 8192, 512, "scale1e8", True),
 }
 
 MERGE_SEED = 107
@@ -78,6 +90,10 @@ def _fill_block(w: Workload, b: int) -> np.ndarray:
         x[u < 0.001] = np.inf
         x[(u >= 0.001) & (u < 0.002)] = -np.inf
         x[(u >= 0.002) & (u < 0.0025)] = np.nan
+    elif w.kind == "plus100":
+        x += np.float32(100.0)
+    elif w.kind == "scale1e8":
+        x *= np.float32(1e-8)
     return x
 
 

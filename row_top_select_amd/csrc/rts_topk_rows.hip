@@ -54,7 +54,10 @@ struct RowTraits<true> {
 
 constexpr int kVec = 4;             // elements per lane per chunk
 constexpr int kChunk = kWave * kVec;  // elements per chunk
-constexpr int kGroup = 4;           // chunks per group (one group in flight)
+// Chunks per load group: 4 KB per wave in flight either way (16 B per lane
+// for fp32, 8 B for bf16).
+template <bool BF16>
+constexpr int kGroupOf = BF16 ? 8 : 4;
 
 template <bool BF16>
 __device__ __forceinline__ uint32_t load_bits(const typename RowTraits<BF16>::elem* p) {
@@ -196,6 +199,7 @@ void topk_rows_stream_kernel(
     int32_t groups) {
     using T = typename RowTraits<BF16>::elem;
     using V = typename RowTraits<BF16>::vec;
+    constexpr int kGroup = kGroupOf<BF16>;
     constexpr int LP = kWave * E;
     constexpr int SCAP = kWave * ES;            // room for new survivors
     constexpr int SBUF = SCAP > LP ? SCAP : LP;  // also carries the selected list into L

@@ -38,3 +38,14 @@ def test_rank_slices():
     s = datagen.rank_slices(g, 8)
     assert s.shape == (8, 2, 3)
     assert s[3, 1].tolist() == [27.0, 35.0, 43.0]
+
+
+def test_robust_workloads_share_one_base():
+    import numpy as np
+    base = datagen.logits(datagen.WORKLOADS["robust"], blocks=[7])
+    plus = datagen.logits(datagen.WORKLOADS["robust_plus100"], blocks=[7])
+    scal = datagen.logits(datagen.WORKLOADS["robust_scale1e8"], blocks=[7])
+    assert np.array_equal(plus, base + np.float32(100.0))
+    assert np.array_equal(scal, base * np.float32(1e-8))
+    ends = datagen.row_ends(datagen.WORKLOADS["robust"])
+    assert ends[0] == 1 and ends[-1] == 8192

@@ -214,3 +214,32 @@ def test_verylong_config_sampled(rts):
     assert (got < ends[:, None]).all()
     vals = np.take_along_axis(x, got.astype(np.int64), axis=1)
     assert (np.diff(vals, axis=1) <= 0).all()
+
+
+# Distribution robustness (the pages' ablation at 8K queries x 8K keys: the same
+# normal values, then +100 and *1e-8, which concentrate the scores; causal rows
+# i + 1 long, so the first 511 rows end in -1 tails).  Full parity on every row.
+@pytest.mark.parametrize("name", ["robust", "robust_plus100", "robust_scale1e8"])
+def test_distribution_robustness(rts, name):
+    w = datagen.WORKLOADS[name]
+    say("robust", w)
+    x = datagen.logits(w)
+    ends = datagen.row_ends(w)
+    got = run_gpu(rts, x, ends, w.k)
+    assert_ids_equal(got, oracle.topk_rows(x, ends, w.k), name)
+    assert (got[:w.k - 1, w.k - 1] == -1).all()  # rows shorter than k end in -1
+
+
+def test_verylong_bf16_sampled(rts):
+    # The headline shape in bf16 (its fp32 values rounded to nearest even),
+    # launched as at full size; the oracle checks 128 rows over all blocks.
+    w = datagen.WORKLOADS["verylong"]
+    say("verylong bf16 generate")
+    xb = datagen.bf16_bits(datagen.logits(w))
+    ends = datagen.row_ends(w)
+    say("verylong bf16 run")
+    got = host(rts.topk_rows(bf16_dev(xb), w.k, row_ends=dev(ends)))
+    sample = np.arange(5, w.rows, 32)
+    exp = oracle.topk_rows(np.ascontiguousarray(xb[sample]), ends[sample], w.k)
+    assert_ids_equal(got[sample], exp, "verylong bf16 sampled rows")
+    assert (got >= 0).all() and (got < ends[:, None]).all()
