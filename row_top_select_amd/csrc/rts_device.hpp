@@ -278,4 +278,40 @@ __device__ __forceinline__ uint32_t wave_incl_scan32(uint32_t v) {
     return v;
 }
 
+// ---------------------------------------------------------------------------
+// Radix-select step over 256 wave-private LDS bins (bin b counts the entries of
+// its digit).
+// ---------------------------------------------------------------------------
+// Scans the bins from the top: finds the bin where the running count reaches
+// need, lowers need by the count above it and returns the bin and its count
+// (uniform).  False only if the counts were inconsistent.
+__device__ __forceinline__ bool radix_find(const uint32_t* hist, int& need, uint32_t& bin,
+                                           uint32_t& cb) {
+    const int lane = lane_id();
+    uint32_t c[4];  // lane l owns bins 255-4l .. 252-4l
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = hist[255 - 4 * lane - j];
+    const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+    uint32_t run = wave_incl_scan32(tot) - tot;
+    int fj = -1;
+    uint32_t above = 0, cl = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (fj < 0 && run < (uint32_t)need && run + c[j] >= (uint32_t)need) {
+            fj = j;
+            above = run;
+            cl = c[j];
+        }
+        run += c[j];
+    }
+    wave_lds_sync();  // the next level clears the bins
+    const uint64_t fm = __ballot(fj >= 0);
+    if (fm == 0ull) return false;
+    const int fl = __ffsll((long long)fm) - 1;
+    bin = 255u - 4u * (uint32_t)fl - (uint32_t)__builtin_amdgcn_readlane(fj, fl);
+    need -= (int)__builtin_amdgcn_readlane(above, fl);
+    cb = __builtin_amdgcn_readlane(cl, fl);
+    return true;
+}
+
 }  // namespace rts

@@ -12,8 +12,11 @@
 //     _decode_key).
 //   * pair select: (score, gid) candidates of the all-gathered [W, R, K, 2]
 //     buffer read in place (PR 65178 Overview and Details).
-// Both selects run one 512-thread workgroup per row with every candidate in
-// registers as a 64-bit composite (key << 32) | (0xFFFFFFFF - gid).  The k-th
+// The packed select runs one wave per row when a row's candidates fit in 64
+// registers per lane and world is a power of two up to 16
+// (merge_packed_wave_kernel); otherwise, and for pairs,
+// one 512-thread workgroup per row holds every candidate in registers as a
+// 64-bit composite (key << 32) | (0xFFFFFFFF - gid).  The k-th
 // composite is found by a radix select whose 256 bins at each level span
 // [min, max] of the composites still in play (so a narrow score range still
 // spreads over the bins); histogram atomics go to 16 lane-striped LDS copies
@@ -356,6 +359,241 @@ __global__ __launch_bounds__(kSelBlock) void merge_packed_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Packed select, one wave per row, no barriers (world * ceil(n/64) <= 64).
+//
+// Lane l holds, for rank r and q = 0 .. qn-1, the word of slot j = q*64 + l in
+// register i = r*qn + q, and bit i of hb holds that slot's plane bit (local
+// bit 16).  Register order then lane order is candidate order (r*n + j), so a
+// running count plus the lane's rank among the register's selected lanes is
+// the output position.
+//   1. ord16 threshold: 256-bin levels over the score half of the words in
+//      [min, max] of the nonzero ones (one level when the scores span fewer
+//      than 256 ord16 values, two at most).
+//   2. Ties at tau16 (the k-th score): the candidates tied there are taken by
+//      ascending gid; up to 64 of them are sorted in one register, more go
+//      through 256-bin levels over the gid.
+//   3. Emission in candidate order, -1 tail; tau16 and the saturation mask
+//      come out of the same pass.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t packed_gid(uint32_t word, uint32_t hibit, uint32_t world, uint32_t r) {
+    const uint32_t local = (0xFFFFu - (word & 0xFFFFu)) | (hibit << 16);
+    return local * world + r;
+}
+
+template <int QN, int W>
+__global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
+    const int32_t* __restrict__ gathered, int32_t world_, int64_t rows, int32_t n, int32_t k,
+    int32_t* __restrict__ out_ids, int32_t* __restrict__ sat_word) {
+    constexpr int NR = QN * W;  // registers: rank r = i / QN, q = i % QN
+    constexpr int32_t world = W;
+    (void)world_;
+    __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+    __shared__ uint32_t tied[kWave];
+    const int lane = lane_id();
+    const int64_t row = blockIdx.x;
+    const int64_t width = (int64_t)n + n / 32;
+
+    uint32_t w[NR];
+    uint32_t hb0 = 0u, hb1 = 0u;  // bit i (hb1: i - 32): the slot's plane bit (local bit 16)
+#pragma unroll
+    for (int r = 0; r < W; ++r) {
+        const int32_t* rp = gathered + ((int64_t)r * rows + row) * width;
+#pragma unroll
+        for (int q = 0; q < QN; ++q) {
+            const int i = r * QN + q;
+            // Only the last register of a rank can reach past n (n % 64 == 32).
+            const bool in = q < QN - 1 || q * kWave + lane < n;
+            const uint32_t word = (uint32_t)rp[in ? q * kWave + lane : 0];
+            // Plane words 2q and 2q+1 cover slots q*64 .. q*64+63: bit `lane`
+            // of their 64-bit concatenation (one uniform load).
+            uint64_t plane = (uint32_t)rp[n + 2 * q];
+            if (q < QN - 1 || q * kWave + 32 < n) plane |= (uint64_t)(uint32_t)rp[n + 2 * q + 1] << 32;
+            w[i] = in ? word : 0u;
+            const uint32_t bit = in ? (uint32_t)(plane >> lane) & 1u : 0u;
+            if (i < 32) hb0 |= bit << i;
+            else hb1 |= bit << (i - 32);
+        }
+    }
+    auto hibit = [&](int i) -> uint32_t { return i < 32 ? (hb0 >> i) & 1u : (hb1 >> (i - 32)) & 1u; };
+    // Each pass recomputes what it derives from w[] (a shift, a compare): kept
+    // from pass to pass, those values would hold ~NR more registers and NR mask
+    // pairs.  An empty asm per register makes every pass start from w[].
+    auto fresh = [&]() {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(w[i]));
+    };
+
+    // Valid count and the ord16 range of the nonzero words (ord16 >= 0x7F
+    // for every packed score, so 0 marks an empty slot).
+    uint32_t nz = 0, mn = 0xFFFFu, mx = 0u;
+    fresh();
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const uint32_t o = w[i] >> 16;
+        nz += (uint32_t)__popcll(__ballot(w[i] != 0u));
+        mn = (w[i] != 0u && o < mn) ? o : mn;
+        mx = o > mx ? o : mx;
+    }
+    mn = wave_min32(mn);
+    mx = wave_max32(mx);
+
+    // Selection rule: ord16 > thr_gt, or ord16 == tie16 and gid <= gid_cut.
+    // Every pass below starts with fresh() outside its (uniform) condition, so
+    // w[] has one version throughout and branches only decide scalars.
+    uint32_t thr_gt = 0u, tie16 = 0u, gid_cut = 0u;
+    uint32_t tau16 = nz == (uint32_t)k ? mn : 0u;  // the k-th selected score (0: fewer than k)
+    bool tau_from_min = false;
+    int need = k;
+    bool open = nz > (uint32_t)k;  // the score threshold is still to be found
+    uint32_t wlo = mn, span = mx - mn;
+    const int bl = span ? 32 - __clz((int)span) : 0;
+    uint32_t sh = bl > 8 ? (uint32_t)(bl - 8) : 0u;
+    bool ties = false;  // the k-th score is tied: take `need` of the tied ones by gid
+    uint32_t ntied = 0u;
+#pragma unroll
+    for (int level = 0; level < 2; ++level) {  // a 16-bit score needs two levels at most
+        fresh();
+        if (open) {
+            *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+            wave_lds_sync();
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const uint32_t x = (w[i] >> 16) - wlo;  // empty: wraps past span
+                if (x <= span)
+                    __hip_atomic_fetch_add(&hist[x >> sh], 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WAVEFRONT);
+            }
+            wave_lds_sync();
+            uint32_t bin, cb;
+            if (!radix_find(hist, need, bin, cb)) {  // only if counts were inconsistent
+                thr_gt = wlo - 1u;
+                tau_from_min = true;
+                open = false;
+            } else {
+                const uint32_t blo = wlo + (bin << sh);
+                if ((int)cb == need) {  // every entry of the bin is taken
+                    thr_gt = blo - 1u;
+                    tau_from_min = sh > 0;
+                    tau16 = blo;
+                    open = false;
+                } else if (sh == 0) {
+                    thr_gt = blo;
+                    tie16 = blo;
+                    tau16 = blo;
+                    ties = true;
+                    ntied = cb;
+                    open = false;
+                } else {
+                    wlo = blo;
+                    const uint32_t top = mx - blo, width1 = (1u << sh) - 1u;
+                    span = width1 < top ? width1 : top;
+                    sh = sh > 8 ? sh - 8 : 0u;
+                }
+            }
+        }
+    }
+    if (open) {  // not reached: two levels always resolve a 16-bit score
+        thr_gt = wlo - 1u;
+        tau_from_min = true;
+    }
+    // Up to 64 tied candidates: sort their gids in one register.
+    fresh();
+    if (ties && ntied <= (uint32_t)kWave) {
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const bool t = (w[i] >> 16) == tie16;
+            const uint64_t m = __ballot(t);
+            if (t) tied[base + (int)mbcnt64(m)] = packed_gid(w[i], hibit(i), (uint32_t)world, (uint32_t)(i / QN));
+            base += (int)__popcll(m);
+        }
+        wave_lds_sync();
+        uint64_t sv[1] = {lane < (int)ntied ? (uint64_t)tied[lane] : ~0ull};
+        wave_bitonic_sort<1, false>(sv);
+        gid_cut = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sv[0], need - 1);
+    }
+    // More: 256-bin levels over key = 2^21-1-gid among the tied candidates.
+    {
+        bool gopen = ties && ntied > (uint32_t)kWave;
+        uint32_t gw = 0u, gspan = (1u << 21) - 1u, gs = 13u;
+#pragma unroll
+        for (int gl = 0; gl < 3; ++gl) {
+            fresh();
+            if (gopen) {
+                *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+                wave_lds_sync();
+#pragma unroll
+                for (int i = 0; i < NR; ++i) {
+                    if ((w[i] >> 16) == tie16) {
+                        const uint32_t key = ((1u << 21) - 1u) -
+                            packed_gid(w[i], hibit(i), (uint32_t)world, (uint32_t)(i / QN));
+                        const uint32_t x = key - gw;
+                        if (x <= gspan)
+                            __hip_atomic_fetch_add(&hist[x >> gs], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WAVEFRONT);
+                    }
+                }
+                wave_lds_sync();
+                uint32_t gbin, gcb;
+                if (!radix_find(hist, need, gbin, gcb)) {
+                    gopen = false;
+                } else {
+                    gw += gbin << gs;
+                    if ((int)gcb == need || gs == 0) {
+                        gopen = false;
+                    } else {
+                        gspan = (1u << gs) - 1u;
+                        gs = gs > 8 ? gs - 8 : 0u;
+                    }
+                }
+            }
+        }
+        if (ties && ntied > (uint32_t)kWave) gid_cut = ((1u << 21) - 1u) - gw;
+    }
+    fresh();
+    if (tau_from_min) {
+        uint32_t t = 0xFFFFu;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const uint32_t o = w[i] >> 16;
+            t = (w[i] != 0u && o > thr_gt && o < t) ? o : t;
+        }
+        tau16 = wave_min32(t);
+    }
+    if (nz <= (uint32_t)k) thr_gt = 0u;  // every nonzero word is selected
+
+    // Emission in candidate order; saturation: rank r keeps its bit iff all n
+    // of its words are nonzero with a score above tau16.
+    int32_t* o_row = out_ids + row * (int64_t)k;
+    int base = 0;
+    uint32_t notsat = 0u;
+    fresh();
+#pragma unroll
+    for (int r = 0; r < W; ++r) {
+        uint64_t bad = 0ull;
+#pragma unroll
+        for (int q = 0; q < QN; ++q) {
+            const int i = r * QN + q;
+            const uint32_t o = w[i] >> 16;
+            const uint32_t gid = packed_gid(w[i], hibit(i), (uint32_t)world, (uint32_t)r);
+            const bool sel = w[i] != 0u && (o > thr_gt || (o == tie16 && gid <= gid_cut));
+            const uint64_t m = __ballot(sel);
+            const int pos = base + (int)mbcnt64(m);
+            if (sel && pos < k) o_row[pos] = (int32_t)gid;
+            base += (int)__popcll(m);
+            bad |= __ballot((q < QN - 1 || q * kWave + lane < n) && (w[i] == 0u || o <= tau16));
+        }
+        if (bad) notsat |= 1u << r;
+    }
+    for (int p = (base < k ? base : k) + lane; p < k; p += kWave) o_row[p] = -1;
+    if (sat_word && lane == 0) {
+        uint32_t mask = ~notsat & ((1u << world) - 1u);
+        if (__popc(mask) > (k - 1) / n) mask = 0u;
+        sat_word[row] = (int32_t)((mask << 16) | tau16);
+    }
+}
+
 template <int KPT>
 __global__ __launch_bounds__(kSelBlock) void merge_pairs_kernel(
     const int32_t* __restrict__ pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
@@ -444,6 +682,45 @@ struct PairsLaunch {
     }
 };
 
+template <int QN, int W>
+void launch_packed_wave(const int32_t* g, int64_t rows, int32_t n, int32_t k, int32_t* ids,
+                        int32_t* sat, hipStream_t s) {
+    if constexpr (QN * W <= 64)
+        hipLaunchKernelGGL((merge_packed_wave_kernel<QN, W>), dim3((unsigned)rows), dim3(kWave), 0,
+                           s, g, W, rows, n, k, ids, sat);
+}
+
+template <int QN>
+bool packed_wave_w(int world, const int32_t* g, int64_t rows, int32_t n, int32_t k, int32_t* ids,
+                   int32_t* sat, hipStream_t s) {
+    if (QN * world > 64) return false;
+    switch (world) {
+        case 1: launch_packed_wave<QN, 1>(g, rows, n, k, ids, sat, s); return true;
+        case 2: launch_packed_wave<QN, 2>(g, rows, n, k, ids, sat, s); return true;
+        case 4: launch_packed_wave<QN, 4>(g, rows, n, k, ids, sat, s); return true;
+        case 8: launch_packed_wave<QN, 8>(g, rows, n, k, ids, sat, s); return true;
+        case 16: launch_packed_wave<QN, 16>(g, rows, n, k, ids, sat, s); return true;
+        default: return false;
+    }
+}
+
+// One wave per row for world in {1, 2, 4, 8, 16} and qn = ceil(n/64) slot
+// registers per rank, with qn * world <= 64; false: use the block kernel.
+bool dispatch_packed_wave(int qn, int world, const int32_t* g, int64_t rows, int32_t n, int32_t k,
+                          int32_t* ids, int32_t* sat, hipStream_t s) {
+    switch (qn) {
+        case 1: return packed_wave_w<1>(world, g, rows, n, k, ids, sat, s);
+        case 2: return packed_wave_w<2>(world, g, rows, n, k, ids, sat, s);
+        case 3: return packed_wave_w<3>(world, g, rows, n, k, ids, sat, s);
+        case 4: return packed_wave_w<4>(world, g, rows, n, k, ids, sat, s);
+        case 5: return packed_wave_w<5>(world, g, rows, n, k, ids, sat, s);
+        case 6: return packed_wave_w<6>(world, g, rows, n, k, ids, sat, s);
+        case 7: return packed_wave_w<7>(world, g, rows, n, k, ids, sat, s);
+        case 8: return packed_wave_w<8>(world, g, rows, n, k, ids, sat, s);
+        default: return false;
+    }
+}
+
 }  // namespace
 
 int launch_pack_candidates(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
@@ -471,6 +748,8 @@ int launch_pack_pairs(const float* x, int64_t rows, int64_t cols, int64_t ld, co
 int launch_merge_packed(const int32_t* gathered, int32_t world, int64_t rows, int32_t n, int32_t k,
                         int32_t* out_ids, int32_t* sat_word, hipStream_t s) {
     if (rows == 0) return RTS_OK;
+    if (dispatch_packed_wave((n + kWave - 1) / kWave, world, gathered, rows, n, k, out_ids, sat_word, s))
+        return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
     const int kpt = pick_kpt((int64_t)world * n);
     const int rc = dispatch_kpt<PackedLaunch>(kpt, gathered, world, rows, n, k, out_ids, sat_word, s);
     if (rc != RTS_OK) return rc;
