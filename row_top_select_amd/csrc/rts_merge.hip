@@ -594,6 +594,267 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pair select: one wave per rank, the `world` waves of a workgroup share a
+// row.  Lane l of wave r holds candidate j = q*64 + l of rank r as a 32-bit
+// score key (0 = empty) and its gid in key[q], gid[q]; wave order, register
+// order, lane order is candidate order.
+//   1. Score threshold: 256-bin levels over the keys in [min, max] of the
+//      valid ones; atomics into 8 lane-striped copies, wave 0 sums them and
+//      finds the bin, three barriers per level.
+//   2. Ties at the k-th key: up to 64 tied candidates are sorted by gid in
+//      wave 0; more go through levels over 2^31-1-gid.
+//   3. Emission: per-wave selected counts, an exclusive scan over the waves,
+//      then running count + mbcnt positions; -1 tail.
+// ---------------------------------------------------------------------------
+constexpr int kPairCopies = 8;
+constexpr int kPairStride = 257;
+
+struct PairSmem {
+    uint32_t hist[kPairCopies][kPairStride];
+    uint32_t bins[256];
+    uint32_t red[16][4];
+    uint32_t bc[4];
+    uint32_t tied[kWave];
+    uint32_t ntied;
+};
+
+// Counts key - wlo (in [0, span]) into bin (key - wlo) >> sh for the entries
+// where `take` holds, then wave 0 finds the bin reaching `need` from the top.
+// Returns (uniform) ok, bin, cb; lowers need.
+template <int QK, typename KeyF>
+__device__ __forceinline__ bool block_radix_level(PairSmem& sm, KeyF keyf, uint32_t wlo,
+                                                  uint32_t span, uint32_t sh, int& need,
+                                                  uint32_t& bin, uint32_t& cb) {
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    uint32_t* hc = sm.hist[lane & (kPairCopies - 1)];
+#pragma unroll
+    for (int q = 0; q < QK; ++q) {
+        uint32_t key;
+        if (keyf(q, key)) {
+            const uint32_t x = key - wlo;
+            if (x <= span)
+                __hip_atomic_fetch_add(&hc[x >> sh], 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < 256; b += blockDim.x) {  // the block may have < 256 threads
+        uint32_t t = 0;
+#pragma unroll
+        for (int c = 0; c < kPairCopies; ++c) {
+            t += sm.hist[c][b];
+            sm.hist[c][b] = 0u;  // clear for the next level
+        }
+        sm.bins[b] = t;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int nd = need;
+        uint32_t b, c;
+        const bool ok = radix_find(sm.bins, nd, b, c);
+        if (lane == 0) {
+            sm.bc[0] = ok ? 1u : 0u;
+            sm.bc[1] = b;
+            sm.bc[2] = c;
+            sm.bc[3] = (uint32_t)nd;
+        }
+    }
+    __syncthreads();
+    const bool ok = sm.bc[0] != 0u;
+    bin = sm.bc[1];
+    cb = sm.bc[2];
+    if (ok) need = (int)sm.bc[3];
+    __syncthreads();  // sm.bc is rewritten by the next level
+    return ok;
+}
+
+template <int QK>
+__global__ __launch_bounds__(1024) void merge_pairs_wave_kernel(
+    const int32_t* __restrict__ pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
+    int32_t* __restrict__ out_ids) {
+    __shared__ PairSmem sm;
+    typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;  // the rank
+    const int64_t row = blockIdx.x;
+    const int nthreads = kWave * world;
+
+    for (int q = threadIdx.x; q < kPairCopies * kPairStride; q += nthreads) (&sm.hist[0][0])[q] = 0u;
+    if (threadIdx.x == 0) sm.ntied = 0u;
+
+    uint32_t key[QK], gid[QK];
+    {
+        const i32x2* src = reinterpret_cast<const i32x2*>(pairs) + ((int64_t)wave * rows + row) * kc;
+#pragma unroll
+        for (int q = 0; q < QK; ++q) {
+            const int j = q * kWave + lane;
+            const bool in = j < kc;  // QK may exceed ceil(kc / 64)
+            const i32x2 pr = src[in ? j : 0];
+            const uint32_t u = (uint32_t)pr[0];
+            const bool valid = in && pr[1] >= 0 && !f32_bits_is_nan(u);
+            key[q] = valid ? key32_of_bits(u) : 0u;
+            gid[q] = (uint32_t)pr[1];
+        }
+    }
+    auto fresh = [&]() {
+#pragma unroll
+        for (int q = 0; q < QK; ++q) asm volatile("" : "+v"(key[q]));
+    };
+
+    // Valid count and key range (every valid key is >= key32(-inf) > 0).
+    uint32_t nv = 0, mn = 0xFFFFFFFFu, mx = 0u;
+    fresh();
+#pragma unroll
+    for (int q = 0; q < QK; ++q) {
+        nv += (uint32_t)__popcll(__ballot(key[q] != 0u));
+        mn = (key[q] != 0u && key[q] < mn) ? key[q] : mn;
+        mx = key[q] > mx ? key[q] : mx;
+    }
+    mn = wave_min32(mn);
+    mx = wave_max32(mx);
+    if (lane == 0) {
+        sm.red[wave][0] = nv;
+        sm.red[wave][1] = mn;
+        sm.red[wave][2] = mx;
+    }
+    __syncthreads();
+    nv = 0;
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+    for (int w = 0; w < world; ++w) {
+        nv += sm.red[w][0];
+        mn = sm.red[w][1] < mn ? sm.red[w][1] : mn;
+        mx = sm.red[w][2] > mx ? sm.red[w][2] : mx;
+    }
+    __syncthreads();
+
+    // Selection rule: key > thr_gt, or key == tie_key and gid <= gid_cut.
+    uint32_t thr_gt = 0u, tie_key = 0u, gid_cut = 0u;
+    if (nv > (uint32_t)k) {
+        int need = k;
+        bool open = true, ties = false;
+        uint32_t wlo = mn, span = mx - mn, ntie = 0u;
+        const int bl = span ? 32 - __clz((int)span) : 0;
+        uint32_t sh = bl > 8 ? (uint32_t)(bl - 8) : 0u;
+#pragma unroll
+        for (int level = 0; level < 4; ++level) {  // a 32-bit key needs four at most
+            fresh();
+            if (open) {
+                uint32_t bin, cb;
+                auto kf = [&](int q, uint32_t& v) { v = key[q]; return true; };
+                if (!block_radix_level<QK>(sm, kf, wlo, span, sh, need, bin, cb)) {
+                    thr_gt = wlo - 1u;
+                    open = false;
+                } else {
+                    const uint32_t blo = wlo + (bin << sh);
+                    if ((int)cb == need) {
+                        thr_gt = blo - 1u;
+                        open = false;
+                    } else if (sh == 0) {
+                        thr_gt = blo;
+                        tie_key = blo;
+                        ties = true;
+                        ntie = cb;
+                        open = false;
+                    } else {
+                        wlo = blo;
+                        const uint32_t top = mx - blo, width1 = (1u << sh) - 1u;
+                        span = width1 < top ? width1 : top;
+                        sh = sh > 8 ? sh - 8 : 0u;
+                    }
+                }
+            }
+        }
+        if (open) thr_gt = wlo - 1u;  // not reached
+        // Ties: up to 64 sorted by gid in wave 0, more through gid levels.
+        fresh();
+        if (ties && ntie <= (uint32_t)kWave) {
+#pragma unroll
+            for (int q = 0; q < QK; ++q) {
+                const bool t = key[q] == tie_key;
+                const uint64_t m = __ballot(t);
+                if (m) {
+                    uint32_t b0 = 0;
+                    if (lane == 0)
+                        b0 = __hip_atomic_fetch_add(&sm.ntied, (uint32_t)__popcll(m), __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+                    b0 = __builtin_amdgcn_readfirstlane(b0);
+                    const uint32_t slot = b0 + mbcnt64(m);
+                    if (t && slot < (uint32_t)kWave) sm.tied[slot] = gid[q];
+                }
+            }
+            __syncthreads();
+            if (wave == 0) {
+                uint64_t sv[1] = {lane < (int)ntie ? (uint64_t)sm.tied[lane] : ~0ull};
+                wave_bitonic_sort<1, false>(sv);
+                const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sv[0], need - 1);
+                if (lane == 0) sm.bc[0] = c;
+            }
+            __syncthreads();
+            gid_cut = sm.bc[0];
+            __syncthreads();
+        }
+        {
+            bool gopen = ties && ntie > (uint32_t)kWave;
+            uint32_t gw = 0u, gspan = 0x7FFFFFFFu, gs = 23u;
+#pragma unroll
+            for (int gl = 0; gl < 4; ++gl) {
+                fresh();
+                if (gopen) {
+                    uint32_t gbin, gcb;
+                    auto kf = [&](int q, uint32_t& v) {
+                        v = 0x7FFFFFFFu - gid[q];
+                        return key[q] == tie_key;
+                    };
+                    if (!block_radix_level<QK>(sm, kf, gw, gspan, gs, need, gbin, gcb)) {
+                        gopen = false;
+                    } else {
+                        gw += gbin << gs;
+                        if ((int)gcb == need || gs == 0) {
+                            gopen = false;
+                        } else {
+                            gspan = (1u << gs) - 1u;
+                            gs = gs > 8 ? gs - 8 : 0u;
+                        }
+                    }
+                }
+            }
+            if (ties && ntie > (uint32_t)kWave) gid_cut = 0x7FFFFFFFu - gw;
+        }
+    }
+
+    // Emission in candidate order.
+    fresh();
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int q = 0; q < QK; ++q) {
+        const bool sel = key[q] != 0u && (key[q] > thr_gt || (key[q] == tie_key && gid[q] <= gid_cut));
+        cnt += (uint32_t)__popcll(__ballot(sel));
+    }
+    if (lane == 0) sm.red[wave][3] = cnt;
+    __syncthreads();
+    uint32_t base = 0, total = 0;
+    for (int w = 0; w < world; ++w) {
+        const uint32_t c = sm.red[w][3];
+        base += w < wave ? c : 0u;
+        total += c;
+    }
+    int32_t* o_row = out_ids + row * (int64_t)k;
+    fresh();
+#pragma unroll
+    for (int q = 0; q < QK; ++q) {
+        const bool sel = key[q] != 0u && (key[q] > thr_gt || (key[q] == tie_key && gid[q] <= gid_cut));
+        const uint64_t m = __ballot(sel);
+        const uint32_t pos = base + mbcnt64(m);
+        if (sel && pos < (uint32_t)k) o_row[pos] = (int32_t)gid[q];
+        base += (uint32_t)__popcll(m);
+    }
+    for (int p = (int)(total < (uint32_t)k ? total : (uint32_t)k) + (int)threadIdx.x; p < k; p += nthreads)
+        o_row[p] = -1;
+}
+
 template <int KPT>
 __global__ __launch_bounds__(kSelBlock) void merge_pairs_kernel(
     const int32_t* __restrict__ pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
@@ -759,6 +1020,20 @@ int launch_merge_packed(const int32_t* gathered, int32_t world, int64_t rows, in
 int launch_merge_pairs(const int32_t* pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
                        int32_t* out_ids, hipStream_t s) {
     if (rows == 0) return RTS_OK;
+    // One wave per rank when a rank's candidates fit in 32 registers per lane.
+    const int qk = (kc + kWave - 1) / kWave;
+    if (qk <= 32 && world <= 16) {
+        const dim3 g((unsigned)rows), b((unsigned)(kWave * world));
+        if (qk <= 4)
+            hipLaunchKernelGGL(merge_pairs_wave_kernel<4>, g, b, 0, s, pairs, world, rows, kc, k, out_ids);
+        else if (qk <= 8)
+            hipLaunchKernelGGL(merge_pairs_wave_kernel<8>, g, b, 0, s, pairs, world, rows, kc, k, out_ids);
+        else if (qk <= 16)
+            hipLaunchKernelGGL(merge_pairs_wave_kernel<16>, g, b, 0, s, pairs, world, rows, kc, k, out_ids);
+        else
+            hipLaunchKernelGGL(merge_pairs_wave_kernel<32>, g, b, 0, s, pairs, world, rows, kc, k, out_ids);
+        return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
+    }
     const int kpt = pick_kpt((int64_t)world * kc);
     const int rc = dispatch_kpt<PairsLaunch>(kpt, pairs, world, rows, kc, k, out_ids, s);
     if (rc != RTS_OK) return rc;
