@@ -51,9 +51,12 @@ def _load():
             lib.oracle_merge_select_rank_major.argtypes = [p, i32, i64, i32, i32, p, p]
             lib.oracle_pack_pairs.argtypes = [p, i64, i64, i64, p, i32, i64, p, i32, i32, p]
             lib.oracle_merge_select_pairs_rank_major.argtypes = [p, i32, i64, i32, i32, p]
+            lib.oracle_merge_rescue_rank_major.argtypes = [p, p, i32, i64, i32, i32, p, p]
+            lib.oracle_rescue_push.argtypes = [p, i32, i32, i64, i32, i32, p, p]
             for f in (lib.oracle_topk_rows, lib.oracle_pack_candidates,
                       lib.oracle_merge_select_rank_major, lib.oracle_pack_pairs,
-                      lib.oracle_merge_select_pairs_rank_major):
+                      lib.oracle_merge_select_pairs_rank_major,
+                      lib.oracle_merge_rescue_rank_major, lib.oracle_rescue_push):
                 f.restype = ctypes.c_int
             lib.oracle_max_threads.restype = ctypes.c_int
             _lib = lib
@@ -163,3 +166,45 @@ def merge_select_pairs_rank_major(pairs, k):
     _check(lib.oracle_merge_select_pairs_rank_major(_ptr(p), world, rows, kc, k, _ptr(ids)),
            "merge_select_pairs_rank_major")
     return ids
+
+
+
+def rescue_slots(n, k):
+    """Receive slots per row: at most (k - 1) // n ranks can be saturated."""
+    return (k - 1) // n
+
+
+def rescue_push(local_packed, rank, world, n, sat_word, recv):
+    """Copy rank ``rank``'s packed local top-k [R, k + k/32] into its receive
+    slot of ``recv`` [R, S, k + k/32] on the rows whose mask has its bit (in place)."""
+    lib = _load()
+    lp = np.ascontiguousarray(local_packed, dtype=np.int32)
+    rows, pw = lp.shape
+    k = pw * 32 // 33
+    assert k + k // 32 == pw and recv.dtype == np.int32 and recv.flags.c_contiguous
+    assert recv.shape == (rows, rescue_slots(n, k), pw)
+    sw = np.ascontiguousarray(sat_word, dtype=np.int32)
+    _check(lib.oracle_rescue_push(_ptr(lp), rank, world, rows, n, k, _ptr(sw), _ptr(recv)),
+           "rescue_push")
+    return recv
+
+
+def merge_rescue_rank_major(gathered, recv, sat_word, ids):
+    """Second round of the packed merge: returns a copy of the round-1 ``ids``
+    [R, k] with every row that enters the second round re-selected.
+
+    ``gathered`` int32 [W, R, n + n/32], ``recv`` int32 [R, (k-1)//n, k + k/32].
+    """
+    lib = _load()
+    g = np.ascontiguousarray(gathered, dtype=np.int32)
+    world, rows, gw = g.shape
+    n = gw * 32 // 33
+    out = np.array(ids, dtype=np.int32, copy=True)
+    k = out.shape[1]
+    assert out.shape == (rows, k)
+    rv = np.ascontiguousarray(recv, dtype=np.int32)
+    assert rv.shape == (rows, rescue_slots(n, k), k + k // 32)
+    sw = np.ascontiguousarray(sat_word, dtype=np.int32)
+    _check(lib.oracle_merge_rescue_rank_major(_ptr(g), _ptr(rv), world, rows, n, k, _ptr(sw),
+                                              _ptr(out)), "merge_rescue_rank_major")
+    return out

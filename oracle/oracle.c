@@ -18,7 +18,8 @@
  *        "Details" (the [W, R, K, 2] (score, global id) buffer read in place).
  *   [P2] vLLM API page vllm.models.kimi_k3.nvidia.ops.dcp_topk_merge.kernels:
  *        module docstring (B' word, bit plane, saturation word),
- *        DCPTopkPackKernel, DCPTopkSelectKernel, _decode_key, _ord16,
+ *        DCPTopkPackKernel, DCPTopkSelectKernel, DCPTopkRescueKernel,
+ *        DCPTopkRescueWorkspace, _decode_key, _ord16,
  *        assert_packed_merge_contract, dcp_topk_pack_indices.
  *   [P3] vLLM pull request 57206, "Use DeepSelect for eligible sparse-indexer
  *        prefill chunks": "Purpose" (causal end bound, KV starts at column 0)
@@ -308,6 +309,113 @@ int oracle_merge_select_rank_major(const int32_t* gathered, int32_t world, int64
     }
     free(buf);
     free(sel);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O3b: second round of the exact packed merge, all W ranks on one     */
+/*      device ([P2] module docstring on exactness, DCPTopkRescueKernel, */
+/*      DCPTopkRescueWorkspace, the select's exact flag)                */
+/* ------------------------------------------------------------------ */
+
+/* A row enters the second round iff its mask is nonzero, names only ranks
+ * below world, and has at most S = (k-1)/n bits (the receive slots per row).
+ * Round 1 never writes any other nonzero mask; such a row is left alone. */
+static int mcand_pos_cmp(const void* pa, const void* pb) {
+    const mcand_t* a = (const mcand_t*)pa;
+    const mcand_t* b = (const mcand_t*)pb;
+    return (a->pos > b->pos) - (a->pos < b->pos);
+}
+
+static int rescue_row_mask(uint32_t sw, int32_t world, int32_t n, int32_t k) {
+    uint32_t mask = sw >> 16;
+    if (mask == 0 || (world < 32 && (mask >> world) != 0)) return 0;
+    if (popcount32(mask) > (k - 1) / n) return 0;
+    return 1;
+}
+
+/* A saturated rank's push: its local top-k of the row, packed into k words
+ * and k/32 plane words, lands in receive slot popc(mask & ((1 << rank) - 1))
+ * of recv [rows, S, k + k/32].  local_packed [rows, k + k/32] is that rank's
+ * pack of its local top-k for every row; only rows whose mask has the rank's
+ * bit are copied. */
+int oracle_rescue_push(const int32_t* local_packed, int32_t rank, int32_t world, int64_t rows,
+                       int32_t n, int32_t k, const int32_t* sat_word, int32_t* recv) {
+    if (world < 1 || world > 16 || rank < 0 || rank >= world || rows < 0 || n < 32 ||
+        n % 32 != 0 || k < 32 || k % 32 != 0)
+        return -1;
+    const int64_t pw = (int64_t)k + k / 32, slots = (k - 1) / n;
+    for (int64_t t = 0; t < rows; ++t) {
+        const uint32_t sw = (uint32_t)sat_word[t];
+        if (!rescue_row_mask(sw, world, n, k) || !(((sw >> 16) >> rank) & 1u)) continue;
+        const int64_t slot = popcount32((sw >> 16) & ((1u << rank) - 1u));
+        memcpy(recv + (t * slots + slot) * pw, local_packed + t * pw, sizeof(int32_t) * (size_t)pw);
+    }
+    return 0;
+}
+
+/* The rescue: for each row that enters the second round, the candidates are,
+ * at flat positions r * n + j, the round-1 words of the ranks whose bit is
+ * clear with ord16 >= tau16 (sat_word's low half), then at W * n + s * k + j
+ * the words of receive slot s, owned by the s-th set bit of the mask.  The
+ * top k under (ord16 desc, gid asc) overwrite out_ids[t] as gids in flat
+ * position order, then -1.  Other rows are not written. */
+int oracle_merge_rescue_rank_major(const int32_t* gathered, const int32_t* recv, int32_t world,
+                                   int64_t rows, int32_t n, int32_t k, const int32_t* sat_word,
+                                   int32_t* out_ids) {
+    if (world < 1 || world > 16 || rows < 0 || n < 32 || n % 32 != 0 || k < 32 || k % 32 != 0)
+        return -1;
+    const int64_t gw = (int64_t)n + n / 32, pw = (int64_t)k + k / 32, slots = (k - 1) / n;
+    const int64_t ncand = (int64_t)world * n + slots * k;
+    mcand_t* buf = (mcand_t*)malloc(sizeof(mcand_t) * (size_t)ncand);
+    if (!buf) return -2;
+    for (int64_t t = 0; t < rows; ++t) {
+        const uint32_t sw = (uint32_t)sat_word[t];
+        if (!rescue_row_mask(sw, world, n, k)) continue;
+        const uint32_t mask = sw >> 16, tau16 = sw & 0xFFFFu;
+        int32_t owner[16];
+        int32_t nsat = 0;
+        for (int32_t r = 0; r < world; ++r)
+            if ((mask >> r) & 1u) owner[nsat++] = r;
+        int64_t cnt = 0;
+        for (int64_t f = 0; f < ncand; ++f) {
+            const int32_t* p;
+            int32_t j, len, r;
+            if (f < (int64_t)world * n) {
+                r = (int32_t)(f / n);
+                j = (int32_t)(f % n);
+                if ((mask >> r) & 1u) continue;
+                p = gathered + ((int64_t)r * rows + t) * gw;
+                len = n;
+            } else {
+                int64_t s = (f - (int64_t)world * n) / k;
+                if (s >= nsat) continue;
+                r = owner[s];
+                j = (int32_t)((f - (int64_t)world * n) % k);
+                p = recv + (t * slots + s) * pw;
+                len = k;
+            }
+            uint32_t w = (uint32_t)p[j];
+            if (w == 0) continue;
+            if (f < (int64_t)world * n && (w >> 16) < tau16) continue;
+            uint32_t plane = (uint32_t)p[len + j / 32];
+            int64_t local = (int64_t)(0xFFFFu - (w & 0xFFFFu)) |
+                            ((int64_t)((plane >> (j % 32)) & 1u) << 16);
+            buf[cnt].o = w >> 16;
+            buf[cnt].gid = local * world + r;
+            buf[cnt].pos = f;
+            ++cnt;
+        }
+        qsort(buf, (size_t)cnt, sizeof(mcand_t), mcand_cmp);
+        const int64_t m = cnt < k ? cnt : k;
+        /* emit the chosen in flat position order */
+        qsort(buf, (size_t)m, sizeof(mcand_t), mcand_pos_cmp);
+        const mcand_t* chosen = buf;
+        int32_t* o = out_ids + t * k;
+        for (int64_t q = 0; q < m; ++q) o[q] = (int32_t)chosen[q].gid;
+        for (int64_t q = m; q < k; ++q) o[q] = -1;
+    }
+    free(buf);
     return 0;
 }
 

@@ -98,3 +98,52 @@ def merge_pairs_row(pairs_row, world, kc, k):
     cands.sort()
     chosen = sorted((pos, gid) for _, gid, pos in cands[:k])
     return [gid for _, gid in chosen] + [-1] * (k - len(chosen))
+
+
+def _decode(words, plane_base, j, rank, world):
+    """(ord16, gid) of slot j of a packed list; plane words start at plane_base."""
+    w = words[j] & 0xFFFFFFFF
+    hi = (words[plane_base + j // 32] >> (j % 32)) & 1
+    return w >> 16, ((0xFFFF - (w & 0xFFFF)) | (hi << 16)) * world + rank
+
+
+def push_row(recv_row, local_row, rank, world, n, k, sat_word):
+    """In place: rank's packed local top-k into its slot when the row is rescued."""
+    mask = (sat_word & 0xFFFFFFFF) >> 16
+    if mask == 0 or mask >> world or bin(mask).count("1") > (k - 1) // n:
+        return
+    if (mask >> rank) & 1:
+        recv_row[bin(mask & ((1 << rank) - 1)).count("1")] = list(local_row)
+
+
+def rescue_row(gathered_row, recv_row, world, n, k, sat_word, ids_row):
+    """Second round of the packed merge for one row.
+
+    gathered_row[r]: rank r's n + n/32 round-1 words; recv_row[s]: receive slot
+    s (k + k/32 words, owned by the s-th saturated rank).  Returns the row's
+    ids: unchanged unless the mask is nonzero, below 1 << world and has at most
+    (k-1)//n bits."""
+    sw = sat_word & 0xFFFFFFFF
+    mask, tau = sw >> 16, sw & 0xFFFF
+    if mask == 0 or mask >> world or bin(mask).count("1") > (k - 1) // n:
+        return list(ids_row)
+    cands = []
+    for r in range(world):
+        if (mask >> r) & 1:
+            continue
+        for j in range(n):
+            if gathered_row[r][j] & 0xFFFFFFFF == 0:
+                continue
+            o, gid = _decode(gathered_row[r], n, j, r, world)
+            if o >= tau:
+                cands.append((-o, gid, r * n + j))
+    owners = [r for r in range(world) if (mask >> r) & 1]
+    for s, r in enumerate(owners):
+        for j in range(k):
+            if recv_row[s][j] & 0xFFFFFFFF == 0:
+                continue
+            o, gid = _decode(recv_row[s], k, j, r, world)
+            cands.append((-o, gid, world * n + s * k + j))
+    cands.sort()
+    chosen = sorted((pos, gid) for _, gid, pos in cands[:k])
+    return [gid for _, gid in chosen] + [-1] * (k - len(chosen))
