@@ -21,6 +21,9 @@ verylong   105   4096 x 102400, N(0,1)         98305 + i           512
 decode     106   64 x 102400, N(0,1)           all 102400          512
 merge      107   global 6710 x 131072 N(0,1);  none                2048
                  rank r owns columns g % 8 == r
+merge_     107   merge + 4.0 on the tokens of  none                2048
+ skew            t % 7 ranks of row t (the
+                 rescue round's input)
 robust     108   8192 x 8192, N(0,1)           i + 1               512
 robust_    108   the same values + 100         i + 1               512
  plus100
@@ -150,6 +153,20 @@ def merge_global(rows: int = MERGE_ROWS, blocks=None, cols: int = MERGE_WORLD * 
     """Global fp32 logits [rows, cols] of the merge workload (row blocks of 1024)."""
     w = Workload("merge", seed, rows, cols, MERGE_K, "normal", False)
     return logits(w, blocks=blocks, threads=threads)
+
+
+MERGE_SKEW_SHIFT = 4.0
+
+
+def skew_ranks(g: np.ndarray, world: int = MERGE_WORLD, shift: float = MERGE_SKEW_SHIFT) -> np.ndarray:
+    """Rank-skewed variant of global logits [R, world * S], in place: in row t
+    the m = t % 7 ranks (t + 3 j) % world, j < m, get ``shift`` added to every
+    token they own, so their local top lists outrank everyone else's and the
+    rows with 1 <= m <= 5 saturate round 1 of the packed merge."""
+    for t in range(g.shape[0]):
+        for j in range(t % 7):
+            g[t, (t + 3 * j) % world::world] += np.float32(shift)
+    return g
 
 
 def rank_slices(g: np.ndarray, world: int = MERGE_WORLD) -> np.ndarray:

@@ -9,8 +9,9 @@
  *        into [W, R, K, 2] and selected in place.
  *   [P2] vLLM API page vllm.models.kimi_k3.nvidia.ops.dcp_topk_merge.kernels:
  *        module docstring (B' word and bit plane, exactness, saturation word),
- *        DCPTopkPackKernel, DCPTopkSelectKernel, _decode_key, _ord16,
- *        dcp_topk_pack_indices, dcp_topk_select, _check_exact.
+ *        DCPTopkPackKernel, DCPTopkSelectKernel, DCPTopkRescueKernel,
+ *        DCPTopkRescueWorkspace, _decode_key, _ord16, dcp_topk_pack_indices,
+ *        dcp_topk_select, _check_exact.
  *   [P3] vLLM pull request 57206, "Use DeepSelect for eligible sparse-indexer
  *        prefill chunks": "Purpose" (causal per-row end, KV from column 0,
  *        preallocated output) and "Test Plan" (short rows, -1 tails, strided
@@ -139,6 +140,47 @@ int pack_candidates(const uint16_t* logits_bf16, int64_t rows, int64_t cols, int
  */
 int merge_select_rank_major(const int32_t* gathered, int32_t world, int64_t rows, int32_t n,
                             int32_t k, int32_t* out_ids, int32_t* sat_word, hipStream_t stream);
+
+/*
+ * Second round of the packed merge, with the world ranks on one device
+ * ([P2] module docstring on exactness, DCPTopkRescueKernel,
+ * DCPTopkRescueWorkspace).  A row enters it iff its sat_word mask is nonzero,
+ * names only ranks below world and has at most S = (k - 1) / n bits (round 1
+ * writes no other nonzero mask); every other row is neither read past its
+ * sat_word nor written.  When S == 0 (n >= k) no row can enter and both calls
+ * return RTS_OK without launching.  The receive buffer
+ *   recv  int32 [rows, S, k + k/32], contiguous
+ * holds, in slot s of row t, the packed local top-k of the s-th saturated
+ * rank (ascending rank order), in the word and plane format of
+ * pack_candidates with n = k.
+ *
+ * rescue_push -- rank `rank`'s push: for every row whose mask enters the
+ * second round and has bit `rank`, copy local_packed[t] (int32 [rows,
+ * k + k/32], contiguous: that rank's pack_candidates of its local top-k) into
+ * recv[t, popc(mask & ((1 << rank) - 1))].  Other slots are not written.
+ * 0 <= rank < world <= 16; n, k positive multiples of 32, k <= 2048.
+ * Errors: RTS_EINVAL, RTS_EUNSUPPORTED, RTS_EHIP.
+ */
+int rescue_push(const int32_t* local_packed, int32_t rank, int32_t world, int64_t rows, int32_t n,
+                int32_t k, const int32_t* sat_word, int32_t* recv, hipStream_t stream);
+
+/*
+ * merge_rescue_rank_major -- the rescue select.  For every row that enters
+ * the second round the candidates are, at flat position r * n + j, the
+ * round-1 words gathered[r, t, j] (layout of merge_select_rank_major) of the
+ * ranks whose bit is clear and whose ord16 >= tau16 (sat_word & 0xFFFF), then
+ * at world * n + s * k + j the words of recv[t, s] for s < popc(mask), owned
+ * by the s-th set bit.  out_ids[t] (int32 [rows, k], contiguous) is
+ * overwritten with the gids of the first min(k, count) under (ord16 desc,
+ * gid asc), in flat position order, then -1.  With the pushes of a valid
+ * round 1 the selected scores equal the top-k of the union as a multiset.
+ * world <= 16; n, k positive multiples of 32, k <= 2048;
+ * world * n + min(S, world) * k <= 32768.
+ * Errors: RTS_EINVAL, RTS_EUNSUPPORTED, RTS_EHIP.
+ */
+int merge_rescue_rank_major(const int32_t* gathered, const int32_t* recv, int32_t world, int64_t rows,
+                            int32_t n, int32_t k, const int32_t* sat_word, int32_t* out_ids,
+                            hipStream_t stream);
 
 /*
  * pack_pairs -- a rank's local top-kc as (score, global id) pairs ([P1]

@@ -3,7 +3,7 @@
 Argument marshalling only: every step runs in the HIP kernels of
 ``librow_top_select.so``.  PyTorch provides device memory and the current
 stream; tensors must live on the GPU.  Importing this package fails loudly if
-the library has not been built (``python -m row_top_select_amd.build``).
+the library has not been built (``python row_top_select_amd/build.py``).
 """
 
 from __future__ import annotations
@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "librow_top_select.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m row_top_select_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python row_top_select_amd/build.py` "
         "(hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -36,8 +36,10 @@ _lib.pack_candidates.argtypes = [_p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p, _
 _lib.merge_select_rank_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p, _p]
 _lib.pack_pairs.argtypes = [_p, _i64, _i64, _i64, _p, _i32, _i64, _p, _i32, _i32, _p, _p]
 _lib.merge_select_pairs_rank_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p]
+_lib.rescue_push.argtypes = [_p, _i32, _i32, _i64, _i32, _i32, _p, _p, _p]
+_lib.merge_rescue_rank_major.argtypes = [_p, _p, _i32, _i64, _i32, _i32, _p, _p, _p]
 for _f in (_lib.topk_rows, _lib.pack_candidates, _lib.merge_select_rank_major, _lib.pack_pairs,
-           _lib.merge_select_pairs_rank_major):
+           _lib.merge_select_pairs_rank_major, _lib.rescue_push, _lib.merge_rescue_rank_major):
     _f.restype = ctypes.c_int
 
 
@@ -172,6 +174,59 @@ def merge_select_rank_major(gathered: torch.Tensor, k: int, out: torch.Tensor | 
                                         _opt(sat_word, "sat_word"), _stream(stream)),
            "merge_select_rank_major")
     return out, sat_word
+
+
+def rescue_slots(n: int, k: int) -> int:
+    """Receive slots per row of the second round: (k - 1) // n."""
+    return (k - 1) // n
+
+
+def _packed_width(t: torch.Tensor, name: str) -> int:
+    w = t.shape[-1]
+    m = w * 32 // 33
+    if m + m // 32 != w:
+        raise ValueError(f"{name}'s last dimension must be m + m/32")
+    return m
+
+
+def rescue_push(local_packed: torch.Tensor, rank: int, world: int, n: int, sat_word: torch.Tensor,
+                recv: torch.Tensor, stream=None) -> torch.Tensor:
+    """Rank ``rank``'s push of its packed local top-k [R, k + k/32] into the
+    receive buffer ``recv`` [R, (k-1)//n, k + k/32] (in place); see the header."""
+    lp = local_packed
+    if lp.dtype != torch.int32 or lp.dim() != 2 or not lp.is_contiguous():
+        raise ValueError("local_packed must be contiguous int32 [R, k + k/32]")
+    rows = lp.shape[0]
+    k = _packed_width(lp, "local_packed")
+    sat_word = _int32_vec(sat_word, rows, "sat_word")
+    if (recv.dtype != torch.int32 or not recv.is_contiguous() or
+            tuple(recv.shape) != (rows, rescue_slots(n, k), k + k // 32)):
+        raise ValueError(f"recv must be contiguous int32 [{rows}, {rescue_slots(n, k)}, {k + k // 32}]")
+    _check(_lib.rescue_push(_dev(lp, "local_packed"), rank, world, rows, n, k,
+                            _dev(sat_word, "sat_word"), _dev(recv, "recv"), _stream(stream)),
+           "rescue_push")
+    return recv
+
+
+def merge_rescue_rank_major(gathered: torch.Tensor, recv: torch.Tensor, sat_word: torch.Tensor,
+                            out: torch.Tensor, stream=None) -> torch.Tensor:
+    """Second round of the packed merge: re-selects, in place in ``out`` [R, k]
+    (round 1's ids), every row whose sat_word enters it; see the header."""
+    if gathered.dtype != torch.int32 or gathered.dim() != 3 or not gathered.is_contiguous():
+        raise ValueError("gathered must be contiguous int32 [W, R, n + n/32]")
+    world, rows, _ = gathered.shape
+    n = _packed_width(gathered, "gathered")
+    if out.dtype != torch.int32 or out.dim() != 2 or out.shape[0] != rows or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous int32 [{rows}, k]")
+    k = out.shape[1]
+    sat_word = _int32_vec(sat_word, rows, "sat_word")
+    if (recv.dtype != torch.int32 or not recv.is_contiguous() or
+            tuple(recv.shape) != (rows, rescue_slots(n, k), k + k // 32)):
+        raise ValueError(f"recv must be contiguous int32 [{rows}, {rescue_slots(n, k)}, {k + k // 32}]")
+    _check(_lib.merge_rescue_rank_major(_dev(gathered, "gathered"), _dev(recv, "recv"), world, rows,
+                                        n, k, _dev(sat_word, "sat_word"), _dev(out, "out"),
+                                        _stream(stream)), "merge_rescue_rank_major")
+    return out
 
 
 def pack_pairs(logits: torch.Tensor, local_idx: torch.Tensor, rank: int, world: int,

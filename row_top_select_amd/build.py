@@ -1,7 +1,9 @@
 """Builds the C-ABI shared library librow_top_select.so for gfx950 with hipcc.
 
-Run as ``python -m row_top_select_amd.build`` (or through
-``__graft_entry__.build()``); the library is written next to this file.
+Run as ``python row_top_select_amd/build.py`` (or through
+``__graft_entry__.build()``); the library is written next to this file.  It
+is run by path, not as a module of the package, because importing the
+package loads the library.
 """
 
 from __future__ import annotations

@@ -85,6 +85,32 @@ int merge_select_rank_major(const int32_t* gathered, int32_t world, int64_t rows
     return rts::launch_merge_packed(gathered, world, rows, n, k, out_ids, sat_word, stream);
 }
 
+int rescue_push(const int32_t* local_packed, int32_t rank, int32_t world, int64_t rows, int32_t n,
+                int32_t k, const int32_t* sat_word, int32_t* recv, hipStream_t stream) {
+    if (world < 1 || world > 16 || rank < 0 || rank >= world || rows < 0 || n < 32 || n % 32 != 0 ||
+        k < 32 || k % 32 != 0)
+        return RTS_EINVAL;
+    if (k > kMaxK || (rows + 3) / 4 > kMaxGrid) return RTS_EUNSUPPORTED;
+    if (rows == 0 || (k - 1) / n == 0) return RTS_OK;
+    if (!local_packed || !sat_word || !recv) return RTS_EINVAL;
+    if (!aligned(local_packed, 4) || !aligned(sat_word, 4) || !aligned(recv, 4)) return RTS_EINVAL;
+    return rts::launch_rescue_push(local_packed, rank, world, rows, n, k, sat_word, recv, stream);
+}
+
+int merge_rescue_rank_major(const int32_t* gathered, const int32_t* recv, int32_t world, int64_t rows,
+                            int32_t n, int32_t k, const int32_t* sat_word, int32_t* out_ids,
+                            hipStream_t stream) {
+    if (world < 1 || world > 16 || rows < 0 || n < 32 || n % 32 != 0 || k < 32 || k % 32 != 0)
+        return RTS_EINVAL;
+    if (k > kMaxK || rts::rescue_candidates(world, n, k) > kMaxCandidates || rows > kMaxGrid)
+        return RTS_EUNSUPPORTED;
+    if (rows == 0 || (k - 1) / n == 0) return RTS_OK;
+    if (!gathered || !recv || !sat_word || !out_ids) return RTS_EINVAL;
+    if (!aligned(gathered, 4) || !aligned(recv, 4) || !aligned(sat_word, 4) || !aligned(out_ids, 4))
+        return RTS_EINVAL;
+    return rts::launch_merge_rescue(gathered, recv, world, rows, n, k, sat_word, out_ids, stream);
+}
+
 int pack_pairs(const float* logits, int64_t rows, int64_t cols, int64_t ld_logits,
                const int32_t* local_idx, int32_t kc, int64_t ld_idx, const int32_t* row_ends,
                int32_t rank, int32_t world, int32_t* pairs, hipStream_t stream) {

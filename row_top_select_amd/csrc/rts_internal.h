@@ -34,6 +34,18 @@ int launch_pack_pairs(const float* x, int64_t rows, int64_t cols, int64_t ld,
 int launch_merge_packed(const int32_t* gathered, int32_t world, int64_t rows, int32_t n,
                         int32_t k, int32_t* out_ids, int32_t* sat_word, hipStream_t stream);
 
+// Candidate slots of one rescued row: world * n round-1 words plus k words
+// for each of at most min((k-1)/n, world) receive slots.
+int rescue_candidates(int32_t world, int32_t n, int32_t k);
+
+int launch_rescue_push(const int32_t* local_packed, int32_t rank, int32_t world, int64_t rows,
+                       int32_t n, int32_t k, const int32_t* sat_word, int32_t* recv,
+                       hipStream_t stream);
+
+int launch_merge_rescue(const int32_t* gathered, const int32_t* recv, int32_t world, int64_t rows,
+                        int32_t n, int32_t k, const int32_t* sat_word, int32_t* out_ids,
+                        hipStream_t stream);
+
 int launch_merge_pairs(const int32_t* pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
                        int32_t* out_ids, hipStream_t stream);
 

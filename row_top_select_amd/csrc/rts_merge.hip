@@ -360,6 +360,104 @@ __global__ __launch_bounds__(kSelBlock) void merge_packed_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Second round of the packed merge (kernels page: module docstring on
+// exactness, DCPTopkRescueKernel, DCPTopkRescueWorkspace), with every rank's
+// push landing in one receive buffer recv [rows, S, k + k/32], S = (k-1)/n.
+//
+// A row takes part iff its mask is nonzero, names only ranks below world and
+// has at most S bits; round 1 writes no other nonzero mask, and other rows are
+// left as they are (a mask check is all they cost).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool rescue_row(uint32_t sw, int32_t world, int32_t slots) {
+    const uint32_t mask = sw >> 16;
+    return mask != 0u && (mask >> world) == 0u && __popc(mask) <= slots;
+}
+
+// The push of one saturated rank: its packed local top-k of the row into
+// receive slot popc(mask & ((1 << rank) - 1)).  One wave per row.
+__global__ __launch_bounds__(256) void rescue_push_kernel(
+    const int32_t* __restrict__ local_packed, int32_t rank, int32_t world, int64_t rows, int32_t n,
+    int32_t k, const int32_t* __restrict__ sat_word, int32_t* __restrict__ recv) {
+    const int64_t row = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+    if (row >= rows) return;
+    const uint32_t sw = (uint32_t)sat_word[row];
+    const int32_t slots = (k - 1) / n;
+    if (!rescue_row(sw, world, slots) || !((sw >> 16) >> rank & 1u)) return;
+    const int64_t pw = (int64_t)k + k / 32;
+    const int64_t slot = __popc((sw >> 16) & ((1u << rank) - 1u));
+    const int32_t* src = local_packed + row * pw;
+    int32_t* dst = recv + (row * slots + slot) * pw;
+    for (int64_t q = lane_id(); q < pw; q += kWave) dst[q] = src[q];
+}
+
+// The rescue select: one workgroup per row.  Flat candidate f = i * kSelBlock
+// + thread: f < world * n is round-1 slot (r, j) = (f / n, f % n), a candidate
+// when rank r is not saturated and its ord16 >= tau16; f >= world * n is slot
+// j of receive slot s, (s, j) = ((f - world*n) / k, (f - world*n) % k), owned
+// by the s-th set bit of the mask.  Selection and emission in flat order are
+// the round-1 block kernel's.
+template <int KPT>
+__global__ __launch_bounds__(kSelBlock) void merge_rescue_kernel(
+    const int32_t* __restrict__ gathered, const int32_t* __restrict__ recv, int32_t world,
+    int64_t rows, int32_t n, int32_t k, const int32_t* __restrict__ sat_word,
+    int32_t* __restrict__ out_ids) {
+    __shared__ SelectSmem sm;
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int32_t slots = (k - 1) / n;
+    const uint32_t sw = (uint32_t)sat_word[row];
+    if (!rescue_row(sw, world, slots)) return;
+    const uint32_t mask = sw >> 16, tau16 = sw & 0xFFFFu;
+    const int32_t nsat = __popc(mask);
+    const int64_t gw = (int64_t)n + n / 32, pw = (int64_t)k + k / 32;
+    const uint32_t r1 = (uint32_t)(world * n);
+    const uint32_t total = r1 + (uint32_t)nsat * (uint32_t)k;
+
+    for (int q = t; q < kHistCopies * kHistStride; q += kSelBlock) (&sm.hist[0][0])[q] = 0u;
+
+    uint64_t key[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        key[i] = 0ull;
+        const uint32_t f = (uint32_t)(i * kSelBlock + t);
+        if (f < r1) {
+            const uint32_t r = f / (uint32_t)n, j = f - r * (uint32_t)n;
+            if (!((mask >> r) & 1u)) {
+                const int32_t* rowp = gathered + ((int64_t)r * rows + row) * gw;
+                const uint32_t word = (uint32_t)rowp[j];
+                if (word != 0u && (word >> 16) >= tau16) {
+                    const uint32_t plane = (uint32_t)rowp[n + (j >> 5)];
+                    const uint32_t local = (0xFFFFu - (word & 0xFFFFu)) | (((plane >> (j & 31)) & 1u) << 16);
+                    key[i] = composite(word >> 16, local * (uint32_t)world + r);
+                }
+            }
+        } else if (f < total) {
+            const uint32_t fr = f - r1, s = fr / (uint32_t)k, j = fr - s * (uint32_t)k;
+            // owner: the s-th set bit of the mask
+            uint32_t m = mask;
+            for (uint32_t c = 0; c < s; ++c) m &= m - 1u;
+            const uint32_t owner = (uint32_t)__builtin_ctz(m);
+            const int32_t* slotp = recv + (row * slots + (int64_t)s) * pw;
+            const uint32_t word = (uint32_t)slotp[j];
+            if (word != 0u) {
+                const uint32_t plane = (uint32_t)slotp[k + (j >> 5)];
+                const uint32_t local = (0xFFFFu - (word & 0xFFFFu)) | (((plane >> (j & 31)) & 1u) << 16);
+                key[i] = composite(word >> 16, local * (uint32_t)world + owner);
+            }
+        }
+    }
+    uint32_t nz = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) nz += key[i] != 0ull;
+    __syncthreads();
+    const uint32_t nvalid = block_sum(nz, sm);
+
+    uint64_t T = 1ull;
+    if (nvalid > (uint32_t)k) T = block_radix_kth<KPT>(key, k, sm);
+    block_emit<KPT>(key, T, k, out_ids + row * (int64_t)k, sm);
+}
+
+// ---------------------------------------------------------------------------
 // Packed select, one wave per row, no barriers (world * ceil(n/64) <= 64).
 //
 // Lane l holds, for rank r and q = 0 .. qn-1, the word of slot j = q*64 + l in
@@ -935,6 +1033,15 @@ struct PackedLaunch {
 };
 
 template <int KPT>
+struct RescueLaunch {
+    static void run(const int32_t* g, const int32_t* recv, int32_t world, int64_t rows, int32_t n,
+                    int32_t k, const int32_t* sat, int32_t* ids, hipStream_t s) {
+        hipLaunchKernelGGL((merge_rescue_kernel<KPT>), dim3((unsigned)rows), dim3(kSelBlock), 0, s, g,
+                           recv, world, rows, n, k, sat, ids);
+    }
+};
+
+template <int KPT>
 struct PairsLaunch {
     static void run(const int32_t* p, int32_t world, int64_t rows, int32_t kc, int32_t k, int32_t* ids,
                     hipStream_t s) {
@@ -1013,6 +1120,31 @@ int launch_merge_packed(const int32_t* gathered, int32_t world, int64_t rows, in
         return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
     const int kpt = pick_kpt((int64_t)world * n);
     const int rc = dispatch_kpt<PackedLaunch>(kpt, gathered, world, rows, n, k, out_ids, sat_word, s);
+    if (rc != RTS_OK) return rc;
+    return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
+}
+
+int rescue_candidates(int32_t world, int32_t n, int32_t k) {
+    const int32_t slots = (k - 1) / n;
+    return world * n + (slots < world ? slots : world) * k;
+}
+
+int launch_rescue_push(const int32_t* local_packed, int32_t rank, int32_t world, int64_t rows,
+                       int32_t n, int32_t k, const int32_t* sat_word, int32_t* recv, hipStream_t s) {
+    if (rows == 0 || (k - 1) / n == 0) return RTS_OK;
+    const int64_t blocks = (rows + 3) / 4;
+    hipLaunchKernelGGL(rescue_push_kernel, dim3((unsigned)blocks), dim3(256), 0, s, local_packed, rank,
+                       world, rows, n, k, sat_word, recv);
+    return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
+}
+
+int launch_merge_rescue(const int32_t* gathered, const int32_t* recv, int32_t world, int64_t rows,
+                        int32_t n, int32_t k, const int32_t* sat_word, int32_t* out_ids,
+                        hipStream_t s) {
+    if (rows == 0 || (k - 1) / n == 0) return RTS_OK;
+    const int kpt = pick_kpt(rescue_candidates(world, n, k));
+    const int rc = dispatch_kpt<RescueLaunch>(kpt, gathered, recv, world, rows, n, k, sat_word,
+                                              out_ids, s);
     if (rc != RTS_OK) return rc;
     return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
 }

@@ -195,3 +195,135 @@ def test_merge_workload_pipeline_sampled(rts):
             row[r::W] = ranks32[r, t]
         direct = np.argsort(-row, kind="stable")[:K]
         assert set(pids[t].tolist()) == set(direct.tolist())
+
+
+# ---------------------------------------------------------------------------
+# Second round (rescue) of the packed merge
+# ---------------------------------------------------------------------------
+
+def _sat_words(rng, rows, world, n, k, g):
+    """Valid masks with tau16 taken from the row's words, empty masks, and masks
+    that round 1 never writes (too many bits, a bit at or above world)."""
+    slots = (k - 1) // n
+    out = np.zeros(rows, np.uint32)
+    gu = g.view(np.uint32)
+    for t in range(rows):
+        words = gu[:, t, :n].ravel()
+        words = words[words != 0]
+        tau = int(words[rng.integers(0, words.size)]) >> 16 if words.size and t % 3 else \
+            int(rng.integers(0, 1 << 16))
+        kind = t % 6
+        if kind == 0:
+            mask = 0
+        elif kind == 4:
+            mask = (1 << min(world, slots + 1)) - 1 if slots < world else 0
+        elif kind == 5:
+            mask = 1 << world
+        else:
+            nb = int(rng.integers(1, min(slots, world) + 1))
+            mask = sum(1 << int(r) for r in rng.choice(world, size=nb, replace=False))
+        out[t] = ((mask << 16) | tau) & 0xFFFFFFFF
+    return out.view(np.int32)
+
+
+@pytest.mark.parametrize("world,n,k,fill,ties", [
+    (8, 384, 2048, 1.0, False), (8, 384, 2048, 0.7, True), (4, 64, 256, 0.9, False),
+    (2, 32, 64, 1.0, False), (16, 256, 1024, 0.95, True), (3, 96, 2048, 0.8, False),
+    (5, 32, 512, 1.0, True)])
+def test_rescue_random(rts, world, n, k, fill, ties):
+    rng = np.random.default_rng(world * 7919 + n + k)
+    rows, slots = 48, (k - 1) // n
+    g = _gathered(rng, world, rows, n, fill, ties)
+    recv = np.ascontiguousarray(_gathered(rng, slots, rows, k, fill, ties).transpose(1, 0, 2))
+    sw = _sat_words(rng, rows, world, n, k, g)
+    ids0 = rng.integers(-1, 1 << 20, size=(rows, k)).astype(np.int32)
+    say("rescue random", world, n, k, fill, ties)
+    out = dev(ids0)
+    rts.merge_rescue_rank_major(dev(g), dev(recv), dev(sw), out)
+    exp = oracle.merge_rescue_rank_major(g, recv, sw, ids0)
+    assert_ids_equal(host(out), exp, "rescued ids")
+
+
+def test_rescue_push_random(rts):
+    rng = np.random.default_rng(5)
+    world, n, k, rows = 8, 384, 2048, 61
+    slots = (k - 1) // n
+    g = _gathered(rng, world, rows, n, 1.0)
+    sw = _sat_words(rng, rows, world, n, k, g)
+    local = rng.integers(-2**31, 2**31, size=(world, rows, k + k // 32)).astype(np.int32)
+    recv_h = np.full((rows, slots, k + k // 32), 12345, np.int32)
+    recv_d = dev(recv_h)
+    ld = dev(local)
+    swd = dev(sw)
+    for r in range(world):
+        say("rescue push rank", r)
+        rts.rescue_push(ld[r], r, world, n, swd, recv_d)
+        oracle.rescue_push(local[r], r, world, n, sw, recv_h)
+    assert np.array_equal(host(recv_d), recv_h)
+
+
+def test_rescue_limits(rts):
+    g = torch.zeros((16, 4, 33), dtype=torch.int32, device="cuda")
+    sw = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out = torch.zeros((4, 2048), dtype=torch.int32, device="cuda")
+    recv = torch.zeros((4, 63, 2112), dtype=torch.int32, device="cuda")
+    # 16 * 32 + 16 * 2048 candidate slots exceed what one workgroup holds
+    with pytest.raises(rts.RtsError) as e:
+        rts.merge_rescue_rank_major(g, recv, sw, out)
+    assert e.value.status == rts.RTS_EUNSUPPORTED
+    # n >= k: no receive slot, nothing to do
+    g2 = torch.zeros((2, 4, 66), dtype=torch.int32, device="cuda")
+    out2 = torch.full((4, 64), 9, dtype=torch.int32, device="cuda")
+    rts.merge_rescue_rank_major(g2, torch.zeros((4, 0, 66), dtype=torch.int32, device="cuda"),
+                                torch.full((4,), 0x10000, dtype=torch.int32, device="cuda"), out2)
+    assert (host(out2) == 9).all()
+
+
+def test_rescue_workload_pipeline_sampled(rts):
+    # Rank-skewed merge workload (6710 rows, 8 ranks, N = 384, K = 2048): round
+    # 1 on the GPU, every rank's local top-2048 packed and pushed, the rescue;
+    # sampled rows against the oracle's own pipeline, and the pages' exactness
+    # claim (selected scores = top-K of the union) on every sampled row.
+    W, R, S, N, K = (datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_LOCAL_COLS,
+                     datagen.MERGE_N, datagen.MERGE_K)
+    say("rescue workload: generate")
+    g32 = datagen.skew_ranks(datagen.merge_global())
+    ranks16 = datagen.bf16_bits(datagen.rank_slices(g32, W))
+    del g32
+    say("rescue workload: gpu")
+    x16 = bf16_dev(ranks16)
+    gathered = torch.empty((W, R, N + N // 32), dtype=torch.int32, device="cuda")
+    for r in range(W):
+        rts.pack_candidates(x16[r], rts.topk_rows(x16[r], N), out=gathered[r])
+    ids, sat = rts.merge_select_rank_major(gathered, K)
+    ids1 = host(ids).copy()
+    recv = torch.zeros((R, (K - 1) // N, K + K // 32), dtype=torch.int32, device="cuda")
+    local = torch.empty((R, K + K // 32), dtype=torch.int32, device="cuda")
+    for r in range(W):
+        rts.pack_candidates(x16[r], rts.topk_rows(x16[r], K), out=local)
+        rts.rescue_push(local, r, W, N, sat, recv)
+    rts.merge_rescue_rank_major(gathered, recv, sat, ids)
+    ids2, sat_h = host(ids), host(sat)
+    masks = sat_h.view(np.uint32) >> 16
+    assert ((masks != 0).mean() > 0.5), "the skewed workload should saturate most rows"
+    assert np.array_equal(ids2[masks == 0], ids1[masks == 0]), "rows with an empty mask changed"
+
+    sample = np.arange(3, R, 61)
+    say("rescue workload: oracle on", len(sample), "rows")
+    sub = ranks16[:, sample]
+    o_packed = np.stack([oracle.pack_candidates(sub[r], oracle.topk_rows(sub[r], None, N))
+                         for r in range(W)])
+    o_ids1, o_sat = oracle.merge_select_rank_major(o_packed, K)
+    assert np.array_equal(sat_h[sample], o_sat), "sat_word"
+    o_recv = np.zeros((len(sample), (K - 1) // N, K + K // 32), np.int32)
+    for r in range(W):
+        oracle.rescue_push(oracle.pack_candidates(sub[r], oracle.topk_rows(sub[r], None, K)), r, W, N,
+                           o_sat, o_recv)
+    o_ids2 = oracle.merge_rescue_rank_major(o_packed, o_recv, o_sat, o_ids1)
+    assert_ids_equal(ids2[sample], o_ids2, "rescued ids")
+    vals = datagen.bf16_to_f32(sub)                            # [W, rows, S]
+    for i in range(len(sample)):
+        row = np.empty(W * S, np.float32)
+        for r in range(W):
+            row[r::W] = vals[r, i]
+        assert np.array_equal(np.sort(row[ids2[sample[i]]]), np.sort(row)[-K:]), sample[i]
