@@ -8,7 +8,8 @@ whole matrix, inputs resident in HBM.  Prints one JSON line.
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--all] [--copy-calib]
 
 --all adds the other workloads (prefill, ties, long, decode, the 8K x 8K
-distribution ablation, the headline shape in bf16, packed and pair merges) as a
+distribution ablation, the headline shape in bf16, packed and pair merges, the
+merge's second round) as a
 "secondary" object; --copy-calib only runs a plain 1 GiB device
 copy (the reference point for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling).
 """
@@ -60,6 +61,32 @@ def time_calls(fn, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, ev0.elapsed_time(ev1) / 1e3 / steps
+
+
+def time_graph(fn, steps, torch):
+    """Per-call time of ``fn`` replayed from a HIP graph of ``steps`` calls: for
+    kernels of a few microseconds, where launching from Python one call at a
+    time would be what is measured."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                                       # warm, outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / 1e3 / steps
 
 
 def cpu_baseline(x_sample, ends_sample, k, total_rows_note):
@@ -131,7 +158,35 @@ def secondary(torch, rts, datagen, steps, warmup):
                            "select_algorithmic_GBps": sel_bytes / t_sel / 1e9,
                            "local_top384_bf16_us_per_rank": t_local * 1e6,
                            "pack_us_per_rank": t_pack * 1e6}
+    # Second round.  On this workload no row saturates, so the rescue reads one
+    # sat_word per row; on the rank-skewed variant most rows go through it.
+    slots = (K - 1) // N
+    recv = torch.zeros((R, slots, K + K // 32), dtype=torch.int32, device="cuda")
+    t_fast = time_graph(lambda: rts.merge_rescue_rank_major(gathered, recv, sat, ids), 200, torch)
     del x16
+    gs = datagen.skew_ranks(datagen.merge_global())
+    x16 = torch.from_numpy(datagen.bf16_bits(datagen.rank_slices(gs, W)).view(np.int16)).cuda() \
+        .view(torch.bfloat16)
+    del gs
+    for r in range(W):
+        rts.pack_candidates(x16[r], rts.topk_rows(x16[r], N, out=locs[r]), out=gathered[r])
+    rts.merge_select_rank_major(gathered, K, out=ids, sat_word=sat)
+    local = torch.empty((R, K + K // 32), dtype=torch.int32, device="cuda")
+    lk = torch.empty((R, K), dtype=torch.int32, device="cuda")
+    for r in range(W):
+        rts.pack_candidates(x16[r], rts.topk_rows(x16[r], K, out=lk), out=local)
+        rts.rescue_push(local, r, W, N, sat, recv)
+    t_push = time_graph(lambda: rts.rescue_push(local, W - 1, W, N, sat, recv), 100, torch)
+    _, t_resc = time_calls(lambda: rts.merge_rescue_rank_major(gathered, recv, sat, ids), steps,
+                           warmup, torch)
+    n_sat = int(((sat.cpu().numpy().view(np.uint32) >> 16) != 0).sum())
+    res["merge_rescue"] = {"shape": [W, R, N + N // 32], "recv": [R, slots, K + K // 32], "k": K,
+                           "no_saturated_rows_us": t_fast * 1e6,
+                           "rank_skewed_rows_saturated": n_sat,
+                           "rank_skewed_rescue_us": t_resc * 1e6,
+                           "rank_skewed_rescued_rows_per_s": n_sat / t_resc,
+                           "rank_skewed_push_us_per_rank": t_push * 1e6}
+    del x16, local, lk, recv
     x32 = torch.from_numpy(ranks32).cuda()
     del ranks32
     pairs = torch.empty((W, R, K, 2), dtype=torch.int32, device="cuda")

@@ -390,30 +390,30 @@ __global__ __launch_bounds__(256) void rescue_push_kernel(
     for (int64_t q = lane_id(); q < pw; q += kWave) dst[q] = src[q];
 }
 
-// The rescue select: one workgroup per row.  Flat candidate f = i * kSelBlock
-// + thread: f < world * n is round-1 slot (r, j) = (f / n, f % n), a candidate
-// when rank r is not saturated and its ord16 >= tau16; f >= world * n is slot
-// j of receive slot s, (s, j) = ((f - world*n) / k, (f - world*n) % k), owned
-// by the s-th set bit of the mask.  Selection and emission in flat order are
-// the round-1 block kernel's.
-template <int KPT>
-__global__ __launch_bounds__(kSelBlock) void merge_rescue_kernel(
-    const int32_t* __restrict__ gathered, const int32_t* __restrict__ recv, int32_t world,
-    int64_t rows, int32_t n, int32_t k, const int32_t* __restrict__ sat_word,
-    int32_t* __restrict__ out_ids) {
-    __shared__ SelectSmem sm;
-    const int t = threadIdx.x;
-    const int64_t row = blockIdx.x;
+// The rescue select of one row (all threads of the workgroup).  Flat
+// candidate f = i * kSelBlock + thread: f < world * n is round-1 slot
+// (r, j) = (f / n, f % n), a candidate when rank r is not saturated and its
+// ord16 >= tau16; f >= world * n is slot j of receive slot s,
+// (s, j) = ((f - world*n) / k, (f - world*n) % k), owned by the s-th set bit
+// of the mask.  Selection and emission in flat order are the round-1 block
+// kernel's.
+template <int KPT, bool IN_LOOP>
+__device__ __forceinline__ void rescue_one_row(const int32_t* __restrict__ gathered,
+                                               const int32_t* __restrict__ recv, int32_t world,
+                                               int64_t rows, int32_t n, int32_t k, int64_t row,
+                                               uint32_t sw, int32_t* __restrict__ out_ids,
+                                               SelectSmem& sm) {
+    // Inside a row loop, an opaque copy of the thread index renewed per row:
+    // without it the compiler hoists the per-register slot arithmetic out of
+    // the loop and keeps all of it live across rows.
+    int t = threadIdx.x;
+    if constexpr (IN_LOOP) asm volatile("" : "+v"(t));
     const int32_t slots = (k - 1) / n;
-    const uint32_t sw = (uint32_t)sat_word[row];
-    if (!rescue_row(sw, world, slots)) return;
     const uint32_t mask = sw >> 16, tau16 = sw & 0xFFFFu;
     const int32_t nsat = __popc(mask);
     const int64_t gw = (int64_t)n + n / 32, pw = (int64_t)k + k / 32;
     const uint32_t r1 = (uint32_t)(world * n);
     const uint32_t total = r1 + (uint32_t)nsat * (uint32_t)k;
-
-    for (int q = t; q < kHistCopies * kHistStride; q += kSelBlock) (&sm.hist[0][0])[q] = 0u;
 
     uint64_t key[KPT];
 #pragma unroll
@@ -455,6 +455,67 @@ __global__ __launch_bounds__(kSelBlock) void merge_rescue_kernel(
     uint64_t T = 1ull;
     if (nvalid > (uint32_t)k) T = block_radix_kth<KPT>(key, k, sm);
     block_emit<KPT>(key, T, k, out_ids + row * (int64_t)k, sm);
+    if constexpr (IN_LOOP) __syncthreads();  // block_emit's table is reused by the next row
+}
+
+// One workgroup per row (grid = rows); a row that does not enter returns at once.
+template <int KPT>
+__global__ __launch_bounds__(kSelBlock) void merge_rescue_row_kernel(
+    const int32_t* __restrict__ gathered, const int32_t* __restrict__ recv, int32_t world,
+    int64_t rows, int32_t n, int32_t k, const int32_t* __restrict__ sat_word,
+    int32_t* __restrict__ out_ids) {
+    __shared__ SelectSmem sm;
+    const int64_t row = blockIdx.x;
+    const uint32_t sw = (uint32_t)sat_word[row];
+    if (!rescue_row(sw, world, (k - 1) / n)) return;
+    for (int q = threadIdx.x; q < kHistCopies * kHistStride; q += kSelBlock) (&sm.hist[0][0])[q] = 0u;
+    rescue_one_row<KPT, false>(gathered, recv, world, rows, n, k, row, sw, out_ids, sm);
+}
+
+// Rows dealt to workgroups with stride gridDim.x.  A workgroup reads the
+// sat_words of up to kSelBlock of its rows at once (one per thread), lists
+// those that enter the second round in LDS, then selects them one by one, so
+// a row that does not enter costs one word load and no workgroup launch.
+// Held to 4 waves per SIMD (two workgroups per compute unit).
+template <int KPT>
+__global__ __launch_bounds__(kSelBlock) __attribute__((amdgpu_waves_per_eu(4)))
+void merge_rescue_kernel(const int32_t* __restrict__ gathered, const int32_t* __restrict__ recv,
+                         int32_t world, int64_t rows, int32_t n, int32_t k,
+                         const int32_t* __restrict__ sat_word, int32_t* __restrict__ out_ids) {
+    __shared__ SelectSmem sm;
+    __shared__ uint32_t todo[kSelBlock];
+    __shared__ uint32_t todo_sw[kSelBlock];
+    const int t = threadIdx.x, lane = lane_id(), wave = t / kWave;
+    const int32_t slots = (k - 1) / n;
+    bool hist_clear = false;
+    for (int64_t base = blockIdx.x; base < rows; base += (int64_t)gridDim.x * kSelBlock) {
+        const int64_t my = base + (int64_t)t * gridDim.x;
+        const uint32_t sw = my < rows ? (uint32_t)sat_word[my] : 0u;
+        const bool need = my < rows && rescue_row(sw, world, slots);
+        const uint64_t bal = __ballot(need);
+        if (lane == 0) sm.wsum[wave] = (uint32_t)__popcll(bal);
+        __syncthreads();
+        uint32_t off = 0, cnt = 0;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w) {
+            off += w < wave ? sm.wsum[w] : 0u;
+            cnt += sm.wsum[w];
+        }
+        if (need) {
+            const uint32_t p = off + mbcnt64(bal);
+            todo[p] = (uint32_t)t;
+            todo_sw[p] = sw;
+        }
+        __syncthreads();
+        if (cnt != 0u && !hist_clear) {
+            for (int q = t; q < kHistCopies * kHistStride; q += kSelBlock) (&sm.hist[0][0])[q] = 0u;
+            hist_clear = true;  // every radix level leaves the copies zeroed
+        }
+        for (uint32_t q = 0; q < cnt; ++q) {
+            const int64_t row = base + (int64_t)todo[q] * gridDim.x;
+            rescue_one_row<KPT, true>(gathered, recv, world, rows, n, k, row, todo_sw[q], out_ids, sm);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1032,12 +1093,21 @@ struct PackedLaunch {
     }
 };
 
+// Workgroups of the strided rescue: two per compute unit.
+constexpr int64_t kRescueGrid = 512;
+
 template <int KPT>
 struct RescueLaunch {
     static void run(const int32_t* g, const int32_t* recv, int32_t world, int64_t rows, int32_t n,
                     int32_t k, const int32_t* sat, int32_t* ids, hipStream_t s) {
-        hipLaunchKernelGGL((merge_rescue_kernel<KPT>), dim3((unsigned)rows), dim3(kSelBlock), 0, s, g,
-                           recv, world, rows, n, k, sat, ids);
+        if constexpr (KPT >= 48) {
+            hipLaunchKernelGGL((merge_rescue_row_kernel<KPT>), dim3((unsigned)rows), dim3(kSelBlock), 0,
+                               s, g, recv, world, rows, n, k, sat, ids);
+        } else {
+            const unsigned grid = (unsigned)(rows < kRescueGrid ? rows : kRescueGrid);
+            hipLaunchKernelGGL((merge_rescue_kernel<KPT>), dim3(grid), dim3(kSelBlock), 0, s, g, recv,
+                               world, rows, n, k, sat, ids);
+        }
     }
 };
 

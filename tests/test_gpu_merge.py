@@ -229,7 +229,9 @@ def _sat_words(rng, rows, world, n, k, g):
 @pytest.mark.parametrize("world,n,k,fill,ties", [
     (8, 384, 2048, 1.0, False), (8, 384, 2048, 0.7, True), (4, 64, 256, 0.9, False),
     (2, 32, 64, 1.0, False), (16, 256, 1024, 0.95, True), (3, 96, 2048, 0.8, False),
-    (5, 32, 512, 1.0, True)])
+    (5, 32, 512, 1.0, True),
+    # 48 and 64 candidate registers per thread (one workgroup per row)
+    (16, 1024, 2048, 0.9, False), (16, 128, 2048, 1.0, True)])
 def test_rescue_random(rts, world, n, k, fill, ties):
     rng = np.random.default_rng(world * 7919 + n + k)
     rows, slots = 48, (k - 1) // n
@@ -242,6 +244,32 @@ def test_rescue_random(rts, world, n, k, fill, ties):
     rts.merge_rescue_rank_major(dev(g), dev(recv), dev(sw), out)
     exp = oracle.merge_rescue_rank_major(g, recv, sw, ids0)
     assert_ids_equal(host(out), exp, "rescued ids")
+
+
+def test_rescue_many_rows(rts):
+    # More rows than the strided grid reads in one batch (512 workgroups x 512
+    # sat_words): the rows that enter lie in every batch, the rest stay as given.
+    rng = np.random.default_rng(99)
+    world, n, k, rows = 2, 32, 64, 270000
+    hot = np.unique(np.concatenate([rng.choice(rows, 150, replace=False),
+                                    [0, 511, 512, 262143, 262144, 262145, rows - 1]]))
+    g = np.zeros((world, rows, n + n // 32), np.int32)
+    g[:, hot] = _gathered(rng, world, len(hot), n, 0.9)
+    recv = np.zeros((rows, 1, k + k // 32), np.int32)
+    recv[hot] = _gathered(rng, 1, len(hot), k, 0.9).transpose(1, 0, 2)
+    sw = np.zeros(rows, np.uint32)
+    sw[hot] = ((1 + (hot % 2)) << 16) | 0x8000            # rank 0 or rank 1 saturated
+    sw = sw.view(np.int32)
+    ids0 = np.tile(np.arange(k, dtype=np.int32), (rows, 1))
+    say("rescue many rows", rows, len(hot))
+    out = dev(ids0)
+    rts.merge_rescue_rank_major(dev(g), dev(recv), dev(sw), out)
+    got = host(out)
+    exp_hot = oracle.merge_rescue_rank_major(g[:, hot], recv[hot], sw[hot], ids0[hot])
+    assert_ids_equal(got[hot], exp_hot, "rescued rows")
+    cold = np.ones(rows, bool)
+    cold[hot] = False
+    assert np.array_equal(got[cold], ids0[cold]), "rows with an empty mask changed"
 
 
 def test_rescue_push_random(rts):
