@@ -153,9 +153,23 @@ def secondary(torch, rts, datagen, steps, warmup):
     _, t_sel = time_calls(lambda: rts.merge_select_rank_major(gathered, K, out=ids, sat_word=sat),
                           steps, warmup, torch)
     sel_bytes = W * R * (N + N // 32) * 4 + R * K * 4 + R * 4
+    # The same words reordered row-major [R, W, n + n/32] (the dim-1 gather's
+    # layout): the reorder copy, and the select reading that layout.
+    grm = torch.empty((R, W, N + N // 32), dtype=torch.int32, device="cuda")
+    _, t_copy = time_calls(lambda: grm.copy_(gathered.movedim(0, 1)), steps, warmup, torch)
+    ids_rm = torch.empty_like(ids)
+    sat_rm = torch.empty_like(sat)
+    _, t_sel_rm = time_calls(lambda: rts.merge_select_row_major(grm, K, out=ids_rm, sat_word=sat_rm),
+                             steps, warmup, torch)
+    same = bool(torch.equal(ids_rm, ids) and torch.equal(sat_rm, sat))
+    del grm, ids_rm, sat_rm
     res["merge_packed"] = {"shape": [W, R, N + N // 32], "k": K,
                            "select_us": t_sel * 1e6, "select_rows_per_s": R / t_sel,
                            "select_algorithmic_GBps": sel_bytes / t_sel / 1e9,
+                           "row_major_select_us": t_sel_rm * 1e6,
+                           "reorder_copy_us": t_copy * 1e6,
+                           "reorder_copy_plus_row_major_select_us": (t_copy + t_sel_rm) * 1e6,
+                           "row_major_ids_identical": same,
                            "local_top384_bf16_us_per_rank": t_local * 1e6,
                            "pack_us_per_rank": t_pack * 1e6}
     # Second round.  On this workload no row saturates, so the rescue reads one
@@ -196,9 +210,20 @@ def secondary(torch, rts, datagen, steps, warmup):
     _, t_pairs = time_calls(lambda: rts.merge_select_pairs_rank_major(pairs, K, out=pid), steps,
                             warmup, torch)
     pb = W * R * K * 8 + R * K * 4
+    del x32
+    prm = torch.empty((R, W * K, 2), dtype=torch.int32, device="cuda")
+    _, t_pcopy = time_calls(lambda: prm.view(R, W, K, 2).copy_(pairs.movedim(0, 1)), steps, warmup,
+                            torch)
+    pid_rm = torch.empty_like(pid)
+    _, t_pairs_rm = time_calls(lambda: rts.merge_select_pairs_row_major(prm, K, W, out=pid_rm), steps,
+                               warmup, torch)
     res["merge_pairs"] = {"shape": [W, R, K, 2], "k": K, "select_us": t_pairs * 1e6,
                           "select_rows_per_s": R / t_pairs,
-                          "select_algorithmic_GBps": pb / t_pairs / 1e9}
+                          "select_algorithmic_GBps": pb / t_pairs / 1e9,
+                          "row_major_select_us": t_pairs_rm * 1e6,
+                          "reorder_copy_us": t_pcopy * 1e6,
+                          "reorder_copy_plus_row_major_select_us": (t_pcopy + t_pairs_rm) * 1e6,
+                          "row_major_ids_identical": bool(torch.equal(pid_rm, pid))}
     return res
 
 

@@ -142,6 +142,17 @@ int merge_select_rank_major(const int32_t* gathered, int32_t world, int64_t rows
                             int32_t k, int32_t* out_ids, int32_t* sat_word, hipStream_t stream);
 
 /*
+ * merge_select_row_major -- merge_select_rank_major on the row-major layout
+ * gathered int32 [rows, world, n + n/32] (rank r's words of row t at
+ * gathered[t, r]), the layout an all-gather along dim 1 (or a reorder copy of
+ * the dim-0 result) produces ([P1] Overview, "Before").  Same arguments,
+ * limits, candidate order, outputs and errors; for the same words the outputs
+ * are identical to merge_select_rank_major's.
+ */
+int merge_select_row_major(const int32_t* gathered, int32_t world, int64_t rows, int32_t n, int32_t k,
+                           int32_t* out_ids, int32_t* sat_word, hipStream_t stream);
+
+/*
  * Second round of the packed merge, with the world ranks on one device
  * ([P2] module docstring on exactness, DCPTopkRescueKernel,
  * DCPTopkRescueWorkspace).  A row enters it iff its sat_word mask is nonzero,
@@ -216,6 +227,16 @@ int pack_pairs(const float* logits, int64_t rows, int64_t cols, int64_t ld_logit
  */
 int merge_select_pairs_rank_major(const int32_t* gathered_pairs, int32_t world, int64_t rows,
                                   int32_t kc, int32_t k, int32_t* out_ids, hipStream_t stream);
+
+/*
+ * merge_select_pairs_row_major -- merge_select_pairs_rank_major on the
+ * row-major layout gathered_pairs int32 [rows, world * kc, 2] (candidate
+ * r * kc + j of row t is rank r's slot j), the [R, W*K, 2] buffer of [P1]
+ * Overview, "Before".  Same arguments, limits, order and errors; for the same
+ * pairs the ids are identical to merge_select_pairs_rank_major's.
+ */
+int merge_select_pairs_row_major(const int32_t* gathered_pairs, int32_t world, int64_t rows,
+                                 int32_t kc, int32_t k, int32_t* out_ids, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -36,10 +36,13 @@ _lib.pack_candidates.argtypes = [_p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p, _
 _lib.merge_select_rank_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p, _p]
 _lib.pack_pairs.argtypes = [_p, _i64, _i64, _i64, _p, _i32, _i64, _p, _i32, _i32, _p, _p]
 _lib.merge_select_pairs_rank_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p]
+_lib.merge_select_row_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p, _p]
+_lib.merge_select_pairs_row_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p]
 _lib.rescue_push.argtypes = [_p, _i32, _i32, _i64, _i32, _i32, _p, _p, _p]
 _lib.merge_rescue_rank_major.argtypes = [_p, _p, _i32, _i64, _i32, _i32, _p, _p, _p]
 for _f in (_lib.topk_rows, _lib.pack_candidates, _lib.merge_select_rank_major, _lib.pack_pairs,
-           _lib.merge_select_pairs_rank_major, _lib.rescue_push, _lib.merge_rescue_rank_major):
+           _lib.merge_select_pairs_rank_major, _lib.rescue_push, _lib.merge_rescue_rank_major,
+           _lib.merge_select_row_major, _lib.merge_select_pairs_row_major):
     _f.restype = ctypes.c_int
 
 
@@ -226,6 +229,45 @@ def merge_rescue_rank_major(gathered: torch.Tensor, recv: torch.Tensor, sat_word
     _check(_lib.merge_rescue_rank_major(_dev(gathered, "gathered"), _dev(recv, "recv"), world, rows,
                                         n, k, _dev(sat_word, "sat_word"), _dev(out, "out"),
                                         _stream(stream)), "merge_rescue_rank_major")
+    return out
+
+
+def merge_select_row_major(gathered: torch.Tensor, k: int, out: torch.Tensor | None = None,
+                           sat_word: torch.Tensor | None = None, want_sat: bool = True,
+                           stream=None):
+    """The packed select on row-major int32 [R, W, n + n/32]; returns (ids, sat_word)."""
+    if gathered.dtype != torch.int32 or gathered.dim() != 3 or not gathered.is_contiguous():
+        raise ValueError("gathered must be contiguous int32 [R, W, n + n/32]")
+    rows, world, _ = gathered.shape
+    n = _packed_width(gathered, "gathered")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=gathered.device)
+    if out.dtype != torch.int32 or tuple(out.shape) != (rows, k) or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous int32 [{rows}, {k}]")
+    if sat_word is None and want_sat:
+        sat_word = torch.empty((rows,), dtype=torch.int32, device=gathered.device)
+    _check(_lib.merge_select_row_major(_dev(gathered, "gathered"), world, rows, n, k, _dev(out, "out"),
+                                       _opt(sat_word, "sat_word"), _stream(stream)),
+           "merge_select_row_major")
+    return out, sat_word
+
+
+def merge_select_pairs_row_major(gathered_pairs: torch.Tensor, k: int, world: int,
+                                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The pair select on row-major int32 [R, W * kc, 2]; returns ids [R, k]."""
+    g = gathered_pairs
+    if g.dtype != torch.int32 or g.dim() != 3 or g.shape[2] != 2 or not g.is_contiguous():
+        raise ValueError("gathered_pairs must be contiguous int32 [R, W * kc, 2]")
+    rows, wkc, _ = g.shape
+    if world < 1 or wkc % world != 0:
+        raise ValueError("the candidate dimension must be world * kc")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=g.device)
+    if out.dtype != torch.int32 or tuple(out.shape) != (rows, k) or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous int32 [{rows}, {k}]")
+    _check(_lib.merge_select_pairs_row_major(_dev(g, "gathered_pairs"), world, rows, wkc // world, k,
+                                             _dev(out, "out"), _stream(stream)),
+           "merge_select_pairs_row_major")
     return out
 
 

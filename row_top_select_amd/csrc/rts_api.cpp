@@ -74,15 +74,38 @@ int pack_candidates(const uint16_t* logits_bf16, int64_t rows, int64_t cols, int
                                        row_ends, packed, stream);
 }
 
-int merge_select_rank_major(const int32_t* gathered, int32_t world, int64_t rows, int32_t n,
-                            int32_t k, int32_t* out_ids, int32_t* sat_word, hipStream_t stream) {
+namespace {
+int merge_packed_checked(const int32_t* gathered, bool row_major, int32_t world, int64_t rows,
+                         int32_t n, int32_t k, int32_t* out_ids, int32_t* sat_word,
+                         hipStream_t stream) {
     if (world < 1 || world > 16 || rows < 0 || n < 32 || n % 32 != 0 || k < 1) return RTS_EINVAL;
     if (k > kMaxK || (int64_t)world * n > kMaxCandidates || rows > kMaxGrid) return RTS_EUNSUPPORTED;
     if (rows == 0) return RTS_OK;
     if (!gathered || !out_ids) return RTS_EINVAL;
     if (!aligned(gathered, 4) || !aligned(out_ids, 4) || (sat_word && !aligned(sat_word, 4)))
         return RTS_EINVAL;
-    return rts::launch_merge_packed(gathered, world, rows, n, k, out_ids, sat_word, stream);
+    return rts::launch_merge_packed(gathered, row_major, world, rows, n, k, out_ids, sat_word, stream);
+}
+
+int merge_pairs_checked(const int32_t* gathered_pairs, bool row_major, int32_t world, int64_t rows,
+                        int32_t kc, int32_t k, int32_t* out_ids, hipStream_t stream) {
+    if (world < 1 || rows < 0 || kc < 1 || k < 1) return RTS_EINVAL;
+    if (k > kMaxK || (int64_t)world * kc > kMaxCandidates || rows > kMaxGrid) return RTS_EUNSUPPORTED;
+    if (rows == 0) return RTS_OK;
+    if (!gathered_pairs || !out_ids) return RTS_EINVAL;
+    if (!aligned(gathered_pairs, 8) || !aligned(out_ids, 4)) return RTS_EINVAL;
+    return rts::launch_merge_pairs(gathered_pairs, row_major, world, rows, kc, k, out_ids, stream);
+}
+}  // namespace
+
+int merge_select_rank_major(const int32_t* gathered, int32_t world, int64_t rows, int32_t n,
+                            int32_t k, int32_t* out_ids, int32_t* sat_word, hipStream_t stream) {
+    return merge_packed_checked(gathered, false, world, rows, n, k, out_ids, sat_word, stream);
+}
+
+int merge_select_row_major(const int32_t* gathered, int32_t world, int64_t rows, int32_t n, int32_t k,
+                           int32_t* out_ids, int32_t* sat_word, hipStream_t stream) {
+    return merge_packed_checked(gathered, true, world, rows, n, k, out_ids, sat_word, stream);
 }
 
 int rescue_push(const int32_t* local_packed, int32_t rank, int32_t world, int64_t rows, int32_t n,
@@ -130,12 +153,12 @@ int pack_pairs(const float* logits, int64_t rows, int64_t cols, int64_t ld_logit
 
 int merge_select_pairs_rank_major(const int32_t* gathered_pairs, int32_t world, int64_t rows,
                                   int32_t kc, int32_t k, int32_t* out_ids, hipStream_t stream) {
-    if (world < 1 || rows < 0 || kc < 1 || k < 1) return RTS_EINVAL;
-    if (k > kMaxK || (int64_t)world * kc > kMaxCandidates || rows > kMaxGrid) return RTS_EUNSUPPORTED;
-    if (rows == 0) return RTS_OK;
-    if (!gathered_pairs || !out_ids) return RTS_EINVAL;
-    if (!aligned(gathered_pairs, 8) || !aligned(out_ids, 4)) return RTS_EINVAL;
-    return rts::launch_merge_pairs(gathered_pairs, world, rows, kc, k, out_ids, stream);
+    return merge_pairs_checked(gathered_pairs, false, world, rows, kc, k, out_ids, stream);
+}
+
+int merge_select_pairs_row_major(const int32_t* gathered_pairs, int32_t world, int64_t rows,
+                                 int32_t kc, int32_t k, int32_t* out_ids, hipStream_t stream) {
+    return merge_pairs_checked(gathered_pairs, true, world, rows, kc, k, out_ids, stream);
 }
 
 }  // extern "C"

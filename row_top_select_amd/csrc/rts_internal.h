@@ -31,8 +31,10 @@ int launch_pack_pairs(const float* x, int64_t rows, int64_t cols, int64_t ld,
                       const int32_t* row_ends, int32_t rank, int32_t world, int32_t* pairs,
                       hipStream_t stream);
 
-int launch_merge_packed(const int32_t* gathered, int32_t world, int64_t rows, int32_t n,
-                        int32_t k, int32_t* out_ids, int32_t* sat_word, hipStream_t stream);
+// row_major: gathered is [rows, world, n + n/32] instead of [world, rows, n + n/32].
+int launch_merge_packed(const int32_t* gathered, bool row_major, int32_t world, int64_t rows,
+                        int32_t n, int32_t k, int32_t* out_ids, int32_t* sat_word,
+                        hipStream_t stream);
 
 // Candidate slots of one rescued row: world * n round-1 words plus k words
 // for each of at most min((k-1)/n, world) receive slots.
@@ -46,7 +48,8 @@ int launch_merge_rescue(const int32_t* gathered, const int32_t* recv, int32_t wo
                         int32_t n, int32_t k, const int32_t* sat_word, int32_t* out_ids,
                         hipStream_t stream);
 
-int launch_merge_pairs(const int32_t* pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
-                       int32_t* out_ids, hipStream_t stream);
+// row_major: pairs is [rows, world * kc, 2] instead of [world, rows, kc, 2].
+int launch_merge_pairs(const int32_t* pairs, bool row_major, int32_t world, int64_t rows,
+                       int32_t kc, int32_t k, int32_t* out_ids, hipStream_t stream);
 
 }  // namespace rts

@@ -35,6 +35,15 @@ constexpr int kHistCopies = 16;
 constexpr int kHistStride = 257;
 constexpr int kMaxTab = 64 * kSelWaves;  // KPT * waves entries of the emission table
 
+// Where rank r's candidates of row t start, in units of one rank-row (n + n/32
+// words, or kc pairs): r * rank_stride + t * row_stride.  Rank-major
+// [W, R, .] (the dim-0 all-gather read in place) is {rows, 1}; row-major
+// [R, W, .] (the reordered buffer) is {1, W}.
+struct Layout {
+    int64_t rank_stride, row_stride;
+    __host__ __device__ int64_t at(int64_t r, int64_t row) const { return r * rank_stride + row * row_stride; }
+};
+
 struct SelectSmem {
     uint32_t hist[kHistCopies][kHistStride];
     uint32_t bins[256];
@@ -285,8 +294,8 @@ struct FlatWalk {
 
 template <int KPT>
 __global__ __launch_bounds__(kSelBlock) void merge_packed_kernel(
-    const int32_t* __restrict__ gathered, int32_t world, int64_t rows, int32_t n, int32_t k,
-    int32_t* __restrict__ out_ids, int32_t* __restrict__ sat_word) {
+    const int32_t* __restrict__ gathered, Layout lay, int32_t world, int64_t rows, int32_t n,
+    int32_t k, int32_t* __restrict__ out_ids, int32_t* __restrict__ sat_word) {
     __shared__ SelectSmem sm;
     const int t = threadIdx.x, lane = lane_id();
     const int64_t row = blockIdx.x;
@@ -303,7 +312,7 @@ __global__ __launch_bounds__(kSelBlock) void merge_packed_kernel(
         for (int i = 0; i < KPT; ++i) {
             key[i] = 0ull;
             if (i * kSelBlock + t < total) {
-                const int32_t* rowp = gathered + ((int64_t)w.r * rows + row) * width;
+                const int32_t* rowp = gathered + lay.at(w.r, row) * width;
                 const uint32_t word = (uint32_t)rowp[w.j];
                 const uint32_t plane = (uint32_t)rowp[n + (w.j >> 5)];
                 if (word != 0u) {
@@ -542,8 +551,8 @@ __device__ __forceinline__ uint32_t packed_gid(uint32_t word, uint32_t hibit, ui
 
 template <int QN, int W>
 __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
-    const int32_t* __restrict__ gathered, int32_t world_, int64_t rows, int32_t n, int32_t k,
-    int32_t* __restrict__ out_ids, int32_t* __restrict__ sat_word) {
+    const int32_t* __restrict__ gathered, Layout lay, int32_t world_, int64_t rows, int32_t n,
+    int32_t k, int32_t* __restrict__ out_ids, int32_t* __restrict__ sat_word) {
     constexpr int NR = QN * W;  // registers: rank r = i / QN, q = i % QN
     constexpr int32_t world = W;
     (void)world_;
@@ -557,7 +566,7 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
     uint32_t hb0 = 0u, hb1 = 0u;  // bit i (hb1: i - 32): the slot's plane bit (local bit 16)
 #pragma unroll
     for (int r = 0; r < W; ++r) {
-        const int32_t* rp = gathered + ((int64_t)r * rows + row) * width;
+        const int32_t* rp = gathered + lay.at(r, row) * width;
 #pragma unroll
         for (int q = 0; q < QN; ++q) {
             const int i = r * QN + q;
@@ -831,8 +840,8 @@ __device__ __forceinline__ bool block_radix_level(PairSmem& sm, KeyF keyf, uint3
 
 template <int QK>
 __global__ __launch_bounds__(1024) void merge_pairs_wave_kernel(
-    const int32_t* __restrict__ pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
-    int32_t* __restrict__ out_ids) {
+    const int32_t* __restrict__ pairs, Layout lay, int32_t world, int64_t rows, int32_t kc,
+    int32_t k, int32_t* __restrict__ out_ids) {
     __shared__ PairSmem sm;
     typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
     const int lane = lane_id();
@@ -845,7 +854,7 @@ __global__ __launch_bounds__(1024) void merge_pairs_wave_kernel(
 
     uint32_t key[QK], gid[QK];
     {
-        const i32x2* src = reinterpret_cast<const i32x2*>(pairs) + ((int64_t)wave * rows + row) * kc;
+        const i32x2* src = reinterpret_cast<const i32x2*>(pairs) + lay.at(wave, row) * kc;
 #pragma unroll
         for (int q = 0; q < QK; ++q) {
             const int j = q * kWave + lane;
@@ -1016,8 +1025,8 @@ __global__ __launch_bounds__(1024) void merge_pairs_wave_kernel(
 
 template <int KPT>
 __global__ __launch_bounds__(kSelBlock) void merge_pairs_kernel(
-    const int32_t* __restrict__ pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
-    int32_t* __restrict__ out_ids) {
+    const int32_t* __restrict__ pairs, Layout lay, int32_t world, int64_t rows, int32_t kc,
+    int32_t k, int32_t* __restrict__ out_ids) {
     __shared__ SelectSmem sm;
     typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
     const int t = threadIdx.x;
@@ -1034,7 +1043,7 @@ __global__ __launch_bounds__(kSelBlock) void merge_pairs_kernel(
             key[i] = 0ull;
             if (i * kSelBlock + t < total) {
                 const i32x2 pr =
-                    reinterpret_cast<const i32x2*>(pairs)[((int64_t)w.r * rows + row) * kc + w.j];
+                    reinterpret_cast<const i32x2*>(pairs)[lay.at(w.r, row) * kc + w.j];
                 const uint32_t u = (uint32_t)pr[0];
                 if (pr[1] >= 0 && !f32_bits_is_nan(u)) key[i] = composite(key32_of_bits(u), (uint32_t)pr[1]);
             }
@@ -1086,10 +1095,10 @@ int dispatch_kpt(int kpt, A... args) {
 
 template <int KPT>
 struct PackedLaunch {
-    static void run(const int32_t* g, int32_t world, int64_t rows, int32_t n, int32_t k, int32_t* ids,
-                    int32_t* sat, hipStream_t s) {
+    static void run(const int32_t* g, Layout lay, int32_t world, int64_t rows, int32_t n, int32_t k,
+                    int32_t* ids, int32_t* sat, hipStream_t s) {
         hipLaunchKernelGGL((merge_packed_kernel<KPT>), dim3((unsigned)rows), dim3(kSelBlock), 0, s, g,
-                           world, rows, n, k, ids, sat);
+                           lay, world, rows, n, k, ids, sat);
     }
 };
 
@@ -1113,48 +1122,48 @@ struct RescueLaunch {
 
 template <int KPT>
 struct PairsLaunch {
-    static void run(const int32_t* p, int32_t world, int64_t rows, int32_t kc, int32_t k, int32_t* ids,
-                    hipStream_t s) {
+    static void run(const int32_t* p, Layout lay, int32_t world, int64_t rows, int32_t kc, int32_t k,
+                    int32_t* ids, hipStream_t s) {
         hipLaunchKernelGGL((merge_pairs_kernel<KPT>), dim3((unsigned)rows), dim3(kSelBlock), 0, s, p,
-                           world, rows, kc, k, ids);
+                           lay, world, rows, kc, k, ids);
     }
 };
 
 template <int QN, int W>
-void launch_packed_wave(const int32_t* g, int64_t rows, int32_t n, int32_t k, int32_t* ids,
-                        int32_t* sat, hipStream_t s) {
+void launch_packed_wave(const int32_t* g, Layout lay, int64_t rows, int32_t n, int32_t k,
+                        int32_t* ids, int32_t* sat, hipStream_t s) {
     if constexpr (QN * W <= 64)
         hipLaunchKernelGGL((merge_packed_wave_kernel<QN, W>), dim3((unsigned)rows), dim3(kWave), 0,
-                           s, g, W, rows, n, k, ids, sat);
+                           s, g, lay, W, rows, n, k, ids, sat);
 }
 
 template <int QN>
-bool packed_wave_w(int world, const int32_t* g, int64_t rows, int32_t n, int32_t k, int32_t* ids,
-                   int32_t* sat, hipStream_t s) {
+bool packed_wave_w(int world, const int32_t* g, Layout lay, int64_t rows, int32_t n, int32_t k,
+                   int32_t* ids, int32_t* sat, hipStream_t s) {
     if (QN * world > 64) return false;
     switch (world) {
-        case 1: launch_packed_wave<QN, 1>(g, rows, n, k, ids, sat, s); return true;
-        case 2: launch_packed_wave<QN, 2>(g, rows, n, k, ids, sat, s); return true;
-        case 4: launch_packed_wave<QN, 4>(g, rows, n, k, ids, sat, s); return true;
-        case 8: launch_packed_wave<QN, 8>(g, rows, n, k, ids, sat, s); return true;
-        case 16: launch_packed_wave<QN, 16>(g, rows, n, k, ids, sat, s); return true;
+        case 1: launch_packed_wave<QN, 1>(g, lay, rows, n, k, ids, sat, s); return true;
+        case 2: launch_packed_wave<QN, 2>(g, lay, rows, n, k, ids, sat, s); return true;
+        case 4: launch_packed_wave<QN, 4>(g, lay, rows, n, k, ids, sat, s); return true;
+        case 8: launch_packed_wave<QN, 8>(g, lay, rows, n, k, ids, sat, s); return true;
+        case 16: launch_packed_wave<QN, 16>(g, lay, rows, n, k, ids, sat, s); return true;
         default: return false;
     }
 }
 
 // One wave per row for world in {1, 2, 4, 8, 16} and qn = ceil(n/64) slot
 // registers per rank, with qn * world <= 64; false: use the block kernel.
-bool dispatch_packed_wave(int qn, int world, const int32_t* g, int64_t rows, int32_t n, int32_t k,
-                          int32_t* ids, int32_t* sat, hipStream_t s) {
+bool dispatch_packed_wave(int qn, int world, const int32_t* g, Layout lay, int64_t rows, int32_t n,
+                          int32_t k, int32_t* ids, int32_t* sat, hipStream_t s) {
     switch (qn) {
-        case 1: return packed_wave_w<1>(world, g, rows, n, k, ids, sat, s);
-        case 2: return packed_wave_w<2>(world, g, rows, n, k, ids, sat, s);
-        case 3: return packed_wave_w<3>(world, g, rows, n, k, ids, sat, s);
-        case 4: return packed_wave_w<4>(world, g, rows, n, k, ids, sat, s);
-        case 5: return packed_wave_w<5>(world, g, rows, n, k, ids, sat, s);
-        case 6: return packed_wave_w<6>(world, g, rows, n, k, ids, sat, s);
-        case 7: return packed_wave_w<7>(world, g, rows, n, k, ids, sat, s);
-        case 8: return packed_wave_w<8>(world, g, rows, n, k, ids, sat, s);
+        case 1: return packed_wave_w<1>(world, g, lay, rows, n, k, ids, sat, s);
+        case 2: return packed_wave_w<2>(world, g, lay, rows, n, k, ids, sat, s);
+        case 3: return packed_wave_w<3>(world, g, lay, rows, n, k, ids, sat, s);
+        case 4: return packed_wave_w<4>(world, g, lay, rows, n, k, ids, sat, s);
+        case 5: return packed_wave_w<5>(world, g, lay, rows, n, k, ids, sat, s);
+        case 6: return packed_wave_w<6>(world, g, lay, rows, n, k, ids, sat, s);
+        case 7: return packed_wave_w<7>(world, g, lay, rows, n, k, ids, sat, s);
+        case 8: return packed_wave_w<8>(world, g, lay, rows, n, k, ids, sat, s);
         default: return false;
     }
 }
@@ -1183,13 +1192,16 @@ int launch_pack_pairs(const float* x, int64_t rows, int64_t cols, int64_t ld, co
     return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
 }
 
-int launch_merge_packed(const int32_t* gathered, int32_t world, int64_t rows, int32_t n, int32_t k,
-                        int32_t* out_ids, int32_t* sat_word, hipStream_t s) {
+int launch_merge_packed(const int32_t* gathered, bool row_major, int32_t world, int64_t rows,
+                        int32_t n, int32_t k, int32_t* out_ids, int32_t* sat_word, hipStream_t s) {
     if (rows == 0) return RTS_OK;
-    if (dispatch_packed_wave((n + kWave - 1) / kWave, world, gathered, rows, n, k, out_ids, sat_word, s))
+    const Layout lay = row_major ? Layout{1, world} : Layout{rows, 1};
+    if (dispatch_packed_wave((n + kWave - 1) / kWave, world, gathered, lay, rows, n, k, out_ids,
+                             sat_word, s))
         return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
     const int kpt = pick_kpt((int64_t)world * n);
-    const int rc = dispatch_kpt<PackedLaunch>(kpt, gathered, world, rows, n, k, out_ids, sat_word, s);
+    const int rc = dispatch_kpt<PackedLaunch>(kpt, gathered, lay, world, rows, n, k, out_ids,
+                                              sat_word, s);
     if (rc != RTS_OK) return rc;
     return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
 }
@@ -1219,25 +1231,30 @@ int launch_merge_rescue(const int32_t* gathered, const int32_t* recv, int32_t wo
     return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
 }
 
-int launch_merge_pairs(const int32_t* pairs, int32_t world, int64_t rows, int32_t kc, int32_t k,
-                       int32_t* out_ids, hipStream_t s) {
+int launch_merge_pairs(const int32_t* pairs, bool row_major, int32_t world, int64_t rows, int32_t kc,
+                       int32_t k, int32_t* out_ids, hipStream_t s) {
     if (rows == 0) return RTS_OK;
+    const Layout lay = row_major ? Layout{1, world} : Layout{rows, 1};
     // One wave per rank when a rank's candidates fit in 32 registers per lane.
     const int qk = (kc + kWave - 1) / kWave;
     if (qk <= 32 && world <= 16) {
         const dim3 g((unsigned)rows), b((unsigned)(kWave * world));
         if (qk <= 4)
-            hipLaunchKernelGGL(merge_pairs_wave_kernel<4>, g, b, 0, s, pairs, world, rows, kc, k, out_ids);
+            hipLaunchKernelGGL(merge_pairs_wave_kernel<4>, g, b, 0, s, pairs, lay, world, rows, kc, k,
+                               out_ids);
         else if (qk <= 8)
-            hipLaunchKernelGGL(merge_pairs_wave_kernel<8>, g, b, 0, s, pairs, world, rows, kc, k, out_ids);
+            hipLaunchKernelGGL(merge_pairs_wave_kernel<8>, g, b, 0, s, pairs, lay, world, rows, kc, k,
+                               out_ids);
         else if (qk <= 16)
-            hipLaunchKernelGGL(merge_pairs_wave_kernel<16>, g, b, 0, s, pairs, world, rows, kc, k, out_ids);
+            hipLaunchKernelGGL(merge_pairs_wave_kernel<16>, g, b, 0, s, pairs, lay, world, rows, kc, k,
+                               out_ids);
         else
-            hipLaunchKernelGGL(merge_pairs_wave_kernel<32>, g, b, 0, s, pairs, world, rows, kc, k, out_ids);
+            hipLaunchKernelGGL(merge_pairs_wave_kernel<32>, g, b, 0, s, pairs, lay, world, rows, kc, k,
+                               out_ids);
         return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
     }
     const int kpt = pick_kpt((int64_t)world * kc);
-    const int rc = dispatch_kpt<PairsLaunch>(kpt, pairs, world, rows, kc, k, out_ids, s);
+    const int rc = dispatch_kpt<PairsLaunch>(kpt, pairs, lay, world, rows, kc, k, out_ids, s);
     if (rc != RTS_OK) return rc;
     return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
 }

@@ -74,6 +74,33 @@ def test_merge_packed_random(rts, world, n, k, fill, ties):
     assert np.array_equal(host(sat), esat), "sat_word"
 
 
+@pytest.mark.parametrize("world,n,k", [(8, 384, 2048), (3, 96, 500), (16, 64, 1024), (5, 2048, 2048)])
+def test_merge_packed_row_major(rts, world, n, k):
+    # [R, W, n + n/32] holds the same words as [W, R, n + n/32]: same ids and sat_word.
+    rng = np.random.default_rng(world + n + k)
+    g = _gathered(rng, world, 29, n, 0.9, ties=bool(world % 2))
+    say("merge packed row-major", world, n, k)
+    ids, sat = rts.merge_select_row_major(dev(np.ascontiguousarray(g.transpose(1, 0, 2))), k)
+    eids, esat = oracle.merge_select_rank_major(g, k)
+    assert_ids_equal(host(ids), eids, "ids")
+    assert np.array_equal(host(sat), esat), "sat_word"
+
+
+@pytest.mark.parametrize("world,kc,k", [(8, 2048, 2048), (3, 100, 77), (2, 2500, 1024)])
+def test_merge_pairs_row_major(rts, world, kc, k):
+    rng = np.random.default_rng(world * 3 + kc + k)
+    rows = 21
+    p = np.zeros((world, rows, kc, 2), np.int32)
+    p[..., 0] = rng.standard_normal((world, rows, kc)).astype(np.float32).view(np.int32)
+    for t in range(rows):                                  # distinct ids within a row
+        p[:, t, :, 1] = rng.permutation(world * kc * 4)[:world * kc].reshape(world, kc)
+    p[..., 1][rng.random((world, rows, kc)) < 0.05] = -1
+    say("merge pairs row-major", world, kc, k)
+    rm = np.ascontiguousarray(p.transpose(1, 0, 2, 3).reshape(rows, world * kc, 2))
+    got = host(rts.merge_select_pairs_row_major(dev(rm), k, world))
+    assert_ids_equal(got, oracle.merge_select_pairs_rank_major(p, k), "pair ids")
+
+
 def test_merge_packed_saturation_constructed(rts):
     # rank 1 holds every top score: its bit is set, and the output matches the oracle
     world, s, n, k, rows = 8, 2048, 96, 512, 16
@@ -167,6 +194,14 @@ def test_merge_workload_pipeline_sampled(rts):
         loc2 = rts.topk_rows(x32[r], K)
         rts.pack_pairs(x32[r], loc2, r, W, out=pairs[r])
     pids = rts.merge_select_pairs_rank_major(pairs, K)
+    # The reordered (row-major) buffers select the same ids, bit for bit.
+    say("merge workload: row-major")
+    rm_ids, rm_sat = rts.merge_select_row_major(gathered.movedim(0, 1).contiguous(), K)
+    rm_pids = rts.merge_select_pairs_row_major(pairs.movedim(0, 1).reshape(R, W * K, 2).contiguous(),
+                                               K, W)
+    assert torch.equal(rm_ids, ids) and torch.equal(rm_sat, sat), "row-major packed select"
+    assert torch.equal(rm_pids, pids), "row-major pair select"
+    del rm_ids, rm_sat, rm_pids
     ids, sat, pids = host(ids), host(sat), host(pids)
     gpu_locs = np.stack([host(l) for l in locs])
     gpu_packed = host(gathered)
