@@ -53,10 +53,13 @@ def _load():
             lib.oracle_merge_select_pairs_rank_major.argtypes = [p, i32, i64, i32, i32, p]
             lib.oracle_merge_rescue_rank_major.argtypes = [p, p, i32, i64, i32, i32, p, p]
             lib.oracle_rescue_push.argtypes = [p, i32, i32, i64, i32, i32, p, p]
+            lib.oracle_emit_rows.argtypes = [p, i64, i32, i32, i32, p, p, i64, i32, i32, i64, p, i32,
+                                             p]
             for f in (lib.oracle_topk_rows, lib.oracle_pack_candidates,
                       lib.oracle_merge_select_rank_major, lib.oracle_pack_pairs,
                       lib.oracle_merge_select_pairs_rank_major,
-                      lib.oracle_merge_rescue_rank_major, lib.oracle_rescue_push):
+                      lib.oracle_merge_rescue_rank_major, lib.oracle_rescue_push,
+                      lib.oracle_emit_rows):
                 f.restype = ctypes.c_int
             lib.oracle_max_threads.restype = ctypes.c_int
             _lib = lib
@@ -208,3 +211,20 @@ def merge_rescue_rank_major(gathered, recv, sat_word, ids):
     _check(lib.oracle_merge_rescue_rank_major(_ptr(g), _ptr(rv), world, rows, n, k, _ptr(sw),
                                               _ptr(out)), "merge_rescue_rank_major")
     return out
+
+
+def emit_rows(ids, world, dcp_rank, req_id, block_table, block_size, stride_rows, out_cols=None):
+    """This rank's owned physical rows of the selected ``ids`` [R, k]; returns
+    (rows_out [R, out_cols], valid_out [R]).  ``block_table`` int32 [Q, B_max]."""
+    lib = _load()
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    rows, k = ids.shape
+    out_cols = k if out_cols is None else out_cols
+    rq = np.ascontiguousarray(req_id, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    rows_out = np.empty((rows, out_cols), np.int32)
+    valid = np.empty((rows,), np.int32)
+    _check(lib.oracle_emit_rows(_ptr(ids), rows, k, world, dcp_rank, _ptr(rq), _ptr(bt), bt.shape[0],
+                                bt.shape[1], block_size, stride_rows, _ptr(rows_out), out_cols,
+                                _ptr(valid)), "emit_rows")
+    return rows_out, valid

@@ -20,7 +20,8 @@
  *        module docstring (B' word, bit plane, saturation word),
  *        DCPTopkPackKernel, DCPTopkSelectKernel, DCPTopkRescueKernel,
  *        DCPTopkRescueWorkspace, _decode_key, _ord16,
- *        assert_packed_merge_contract, dcp_topk_pack_indices.
+ *        assert_packed_merge_contract, dcp_topk_pack_indices,
+ *        dcp_topk_merge_rows.
  *   [P3] vLLM pull request 57206, "Use DeepSelect for eligible sparse-indexer
  *        prefill chunks": "Purpose" (causal end bound, KV starts at column 0)
  *        and "Test Plan" (short rows, -1 tails, untouched padding).
@@ -500,5 +501,47 @@ int oracle_merge_select_pairs_rank_major(const int32_t* pairs, int32_t world, in
     }
     free(buf);
     free(sel);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O5: a rank's owned physical KV rows of the selected ids ([P2]      */
+/*     DCPTopkSelectKernel docstring on emit_rows, dcp_topk_merge_rows) */
+/* ------------------------------------------------------------------ */
+
+/* For each row t, walk ids[t, 0:k) in order; a gid >= 0 is owned by
+ * dcp_rank when gid % world == dcp_rank.  Its local index local = gid / world
+ * lies in KV block b = local / block_size of request req_id[t]; when b is a
+ * column of the block table (b < table_cols) the token's physical row
+ *   block_table[req_id[t], b] * stride_rows + local % block_size
+ * (wrapped to int32) is appended to rows_out[t].  Then -1 up to out_cols and
+ * valid_out[t] = the number appended.  A req_id outside [0, table_rows)
+ * owns nothing. */
+int oracle_emit_rows(const int32_t* ids, int64_t rows, int32_t k, int32_t world, int32_t dcp_rank,
+                     const int32_t* req_id, const int32_t* block_table, int64_t table_rows,
+                     int32_t table_cols, int32_t block_size, int64_t stride_rows, int32_t* rows_out,
+                     int32_t out_cols, int32_t* valid_out) {
+    if (rows < 0 || k < 1 || world < 1 || dcp_rank < 0 || dcp_rank >= world || table_rows < 0 ||
+        table_cols < 0 || block_size < 1 || out_cols < k)
+        return -1;
+    for (int64_t t = 0; t < rows; ++t) {
+        const int64_t req = req_id[t];
+        int32_t cnt = 0;
+        int32_t* o = rows_out + t * out_cols;
+        if (req >= 0 && req < table_rows) {
+            for (int32_t j = 0; j < k; ++j) {
+                const int32_t gid = ids[t * k + j];
+                if (gid < 0 || gid % world != dcp_rank) continue;
+                const int32_t local = gid / world;
+                const int32_t b = local / block_size;
+                if (b >= table_cols) continue;
+                const int64_t phys = (int64_t)block_table[req * table_cols + b] * stride_rows +
+                                     (local - b * block_size);
+                o[cnt++] = (int32_t)(uint32_t)((uint64_t)phys & 0xFFFFFFFFu);
+            }
+        }
+        valid_out[t] = cnt;
+        for (int32_t j = cnt; j < out_cols; ++j) o[j] = -1;
+    }
     return 0;
 }

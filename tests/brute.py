@@ -147,3 +147,19 @@ def rescue_row(gathered_row, recv_row, world, n, k, sat_word, ids_row):
     cands.sort()
     chosen = sorted((pos, gid) for _, gid, pos in cands[:k])
     return [gid for _, gid in chosen] + [-1] * (k - len(chosen))
+
+
+def emit_rows_row(ids_row, world, dcp_rank, req, table, block_size, stride_rows, out_cols):
+    """One row of a rank's owned physical KV rows: (rows list padded with -1, count).
+    ``table`` is the list of block-table rows (lists of block ids)."""
+    out = []
+    if 0 <= req < len(table):
+        for gid in ids_row:
+            if gid < 0 or gid % world != dcp_rank:
+                continue
+            local = gid // world
+            b, off = divmod(local, block_size)
+            if b < len(table[req]):
+                v = (table[req][b] * stride_rows + off) & 0xFFFFFFFF
+                out.append(v - (1 << 32) if v >= 1 << 31 else v)
+    return out + [-1] * (out_cols - len(out)), len(out)
