@@ -163,6 +163,21 @@ def secondary(torch, rts, datagen, steps, warmup):
                              steps, warmup, torch)
     same = bool(torch.equal(ids_rm, ids) and torch.equal(sat_rm, sat))
     del grm, ids_rm, sat_rm
+    # One rank's owned physical KV rows of the selection (64-token blocks, a
+    # block table of 97 requests x 256 blocks).
+    gen = torch.Generator().manual_seed(7)
+    table = torch.stack([torch.randperm(1 << 18, generator=gen)[:256] for _ in range(97)]) \
+        .to(torch.int32).cuda()
+    req = (torch.arange(R, dtype=torch.int32) % 97).cuda()
+    rows_out = torch.empty((R, K), dtype=torch.int32, device="cuda")
+    valid = torch.empty((R,), dtype=torch.int32, device="cuda")
+    _, t_emit = time_calls(lambda: rts.emit_rows(ids, W, 3, req, table, 64, 64, rows_out=rows_out,
+                                                 valid_out=valid), steps, warmup, torch)
+    emit_bytes = R * K * 4 * 2 + R * 8
+    res["emit_rows"] = {"shape": [R, K], "world": W, "block_size": 64, "us_per_call": t_emit * 1e6,
+                        "owned_rows_per_row": float(valid.float().mean()),
+                        "algorithmic_GBps": emit_bytes / t_emit / 1e9}
+    del rows_out, valid
     res["merge_packed"] = {"shape": [W, R, N + N // 32], "k": K,
                            "select_us": t_sel * 1e6, "select_rows_per_s": R / t_sel,
                            "select_algorithmic_GBps": sel_bytes / t_sel / 1e9,

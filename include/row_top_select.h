@@ -11,7 +11,7 @@
  *        module docstring (B' word and bit plane, exactness, saturation word),
  *        DCPTopkPackKernel, DCPTopkSelectKernel, DCPTopkRescueKernel,
  *        DCPTopkRescueWorkspace, _decode_key, _ord16, dcp_topk_pack_indices,
- *        dcp_topk_select, _check_exact.
+ *        dcp_topk_select, dcp_topk_merge_rows, _check_exact.
  *   [P3] vLLM pull request 57206, "Use DeepSelect for eligible sparse-indexer
  *        prefill chunks": "Purpose" (causal per-row end, KV from column 0,
  *        preallocated output) and "Test Plan" (short rows, -1 tails, strided
@@ -192,6 +192,34 @@ int rescue_push(const int32_t* local_packed, int32_t rank, int32_t world, int64_
 int merge_rescue_rank_major(const int32_t* gathered, const int32_t* recv, int32_t world, int64_t rows,
                             int32_t n, int32_t k, const int32_t* sat_word, int32_t* out_ids,
                             hipStream_t stream);
+
+/*
+ * emit_rows -- this rank's owned physical KV rows of the selected ids ([P2]
+ * DCPTopkSelectKernel docstring on emit_rows, dcp_topk_merge_rows: rows_out,
+ * valid_out), the format sparse attention reads.
+ *
+ * ids         int32 [rows, k], contiguous: global ids as the selects write
+ *             them (negative = empty slot).
+ * world, dcp_rank  0 <= dcp_rank < world: a gid is owned iff
+ *             gid % world == dcp_rank; its local index is gid / world.
+ * req_id      int32 [rows]: the request (block-table row) of each row.
+ * block_table int32 [table_rows, ld_table], first table_cols columns used:
+ *             KV block ids of each request.
+ * block_size  tokens per KV block (>= 1); stride_rows physical rows per block.
+ * rows_out    int32 [rows, out_cols], contiguous, out_cols >= k: for each
+ *             owned id, in the order ids lists them, the physical row
+ *               block_table[req, b] * stride_rows + local % block_size,
+ *             b = local / block_size (computed in 64 bits, stored as its low
+ *             32 bits); then -1.  An id whose block b >= table_cols is
+ *             dropped; a row whose req_id is outside [0, table_rows) owns
+ *             nothing.
+ * valid_out   int32 [rows]: the number of rows written for each row.
+ * k <= 2048.  Errors: RTS_EINVAL, RTS_EUNSUPPORTED, RTS_EHIP.
+ */
+int emit_rows(const int32_t* ids, int64_t rows, int32_t k, int32_t world, int32_t dcp_rank,
+              const int32_t* req_id, const int32_t* block_table, int64_t table_rows, int32_t table_cols,
+              int64_t ld_table, int32_t block_size, int64_t stride_rows, int32_t* rows_out,
+              int32_t out_cols, int32_t* valid_out, hipStream_t stream);
 
 /*
  * pack_pairs -- a rank's local top-kc as (score, global id) pairs ([P1]

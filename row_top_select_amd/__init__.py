@@ -38,11 +38,13 @@ _lib.pack_pairs.argtypes = [_p, _i64, _i64, _i64, _p, _i32, _i64, _p, _i32, _i32
 _lib.merge_select_pairs_rank_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p]
 _lib.merge_select_row_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p, _p]
 _lib.merge_select_pairs_row_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p]
+_lib.emit_rows.argtypes = [_p, _i64, _i32, _i32, _i32, _p, _p, _i64, _i32, _i64, _i32, _i64, _p, _i32,
+                           _p, _p]
 _lib.rescue_push.argtypes = [_p, _i32, _i32, _i64, _i32, _i32, _p, _p, _p]
 _lib.merge_rescue_rank_major.argtypes = [_p, _p, _i32, _i64, _i32, _i32, _p, _p, _p]
 for _f in (_lib.topk_rows, _lib.pack_candidates, _lib.merge_select_rank_major, _lib.pack_pairs,
            _lib.merge_select_pairs_rank_major, _lib.rescue_push, _lib.merge_rescue_rank_major,
-           _lib.merge_select_row_major, _lib.merge_select_pairs_row_major):
+           _lib.merge_select_row_major, _lib.merge_select_pairs_row_major, _lib.emit_rows):
     _f.restype = ctypes.c_int
 
 
@@ -269,6 +271,38 @@ def merge_select_pairs_row_major(gathered_pairs: torch.Tensor, k: int, world: in
                                              _dev(out, "out"), _stream(stream)),
            "merge_select_pairs_row_major")
     return out
+
+
+def emit_rows(ids: torch.Tensor, world: int, dcp_rank: int, req_id: torch.Tensor,
+              block_table: torch.Tensor, block_size: int, stride_rows: int,
+              rows_out: torch.Tensor | None = None, valid_out: torch.Tensor | None = None,
+              stream=None):
+    """This rank's owned physical KV rows of ``ids`` [R, k]; returns
+    (rows_out [R, out_cols >= k], valid_out [R]); see emit_rows in the header."""
+    if ids.dtype != torch.int32 or ids.dim() != 2 or not ids.is_contiguous():
+        raise ValueError("ids must be contiguous int32 [R, k]")
+    rows, k = ids.shape
+    req_id = _int32_vec(req_id, rows, "req_id")
+    if req_id is None:
+        raise ValueError("req_id is required")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+            (block_table.shape[1] > 1 and block_table.stride(1) != 1):
+        raise ValueError("block_table must be int32 [Q, B_max] with unit column stride")
+    table_rows, table_cols = block_table.shape
+    ld_table = block_table.stride(0) if table_rows > 1 else table_cols
+    if rows_out is None:
+        rows_out = torch.empty((rows, k), dtype=torch.int32, device=ids.device)
+    if rows_out.dtype != torch.int32 or rows_out.dim() != 2 or rows_out.shape[0] != rows or \
+            rows_out.shape[1] < k or not rows_out.is_contiguous():
+        raise ValueError(f"rows_out must be contiguous int32 [{rows}, >= {k}]")
+    if valid_out is None:
+        valid_out = torch.empty((rows,), dtype=torch.int32, device=ids.device)
+    valid_out = _int32_vec(valid_out, rows, "valid_out")
+    _check(_lib.emit_rows(_dev(ids, "ids"), rows, k, world, dcp_rank, _dev(req_id, "req_id"),
+                          _dev(block_table, "block_table"), table_rows, table_cols, ld_table,
+                          block_size, stride_rows, _dev(rows_out, "rows_out"), rows_out.shape[1],
+                          _dev(valid_out, "valid_out"), _stream(stream)), "emit_rows")
+    return rows_out, valid_out
 
 
 def pack_pairs(logits: torch.Tensor, local_idx: torch.Tensor, rank: int, world: int,

@@ -134,6 +134,25 @@ int merge_rescue_rank_major(const int32_t* gathered, const int32_t* recv, int32_
     return rts::launch_merge_rescue(gathered, recv, world, rows, n, k, sat_word, out_ids, stream);
 }
 
+int emit_rows(const int32_t* ids, int64_t rows, int32_t k, int32_t world, int32_t dcp_rank,
+              const int32_t* req_id, const int32_t* block_table, int64_t table_rows, int32_t table_cols,
+              int64_t ld_table, int32_t block_size, int64_t stride_rows, int32_t* rows_out,
+              int32_t out_cols, int32_t* valid_out, hipStream_t stream) {
+    if (rows < 0 || k < 1 || world < 1 || dcp_rank < 0 || dcp_rank >= world || table_rows < 0 ||
+        table_cols < 0 || ld_table < table_cols || block_size < 1 || out_cols < k)
+        return RTS_EINVAL;
+    if (k > kMaxK || (rows + 3) / 4 > kMaxGrid) return RTS_EUNSUPPORTED;
+    if (rows == 0) return RTS_OK;
+    if (!ids || !req_id || !rows_out || !valid_out || (table_rows > 0 && table_cols > 0 && !block_table))
+        return RTS_EINVAL;
+    if (!aligned(ids, 4) || !aligned(req_id, 4) || !aligned(rows_out, 4) || !aligned(valid_out, 4) ||
+        (block_table && !aligned(block_table, 4)))
+        return RTS_EINVAL;
+    return rts::launch_emit_rows(ids, rows, k, world, dcp_rank, req_id, block_table, table_rows,
+                                 table_cols, ld_table, block_size, stride_rows, rows_out, out_cols,
+                                 valid_out, stream);
+}
+
 int pack_pairs(const float* logits, int64_t rows, int64_t cols, int64_t ld_logits,
                const int32_t* local_idx, int32_t kc, int64_t ld_idx, const int32_t* row_ends,
                int32_t rank, int32_t world, int32_t* pairs, hipStream_t stream) {

@@ -48,6 +48,11 @@ int launch_merge_rescue(const int32_t* gathered, const int32_t* recv, int32_t wo
                         int32_t n, int32_t k, const int32_t* sat_word, int32_t* out_ids,
                         hipStream_t stream);
 
+int launch_emit_rows(const int32_t* ids, int64_t rows, int32_t k, int32_t world, int32_t dcp_rank,
+                     const int32_t* req_id, const int32_t* block_table, int64_t table_rows,
+                     int32_t table_cols, int64_t ld_table, int32_t block_size, int64_t stride_rows,
+                     int32_t* rows_out, int32_t out_cols, int32_t* valid_out, hipStream_t stream);
+
 // row_major: pairs is [rows, world * kc, 2] instead of [world, rows, kc, 2].
 int launch_merge_pairs(const int32_t* pairs, bool row_major, int32_t world, int64_t rows,
                        int32_t kc, int32_t k, int32_t* out_ids, hipStream_t stream);

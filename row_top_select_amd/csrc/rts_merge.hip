@@ -528,6 +528,55 @@ void merge_rescue_kernel(const int32_t* __restrict__ gathered, const int32_t* __
 }
 
 // ---------------------------------------------------------------------------
+// A rank's owned physical KV rows of the selected ids (kernels page:
+// DCPTopkSelectKernel docstring on emit_rows, dcp_topk_merge_rows).  One wave
+// per row: lane l holds ids[t, c*64 + l] in register c; owned ids (gid % W ==
+// dcp_rank, KV block inside the table) are compacted in id order with a
+// ballot prefix, so the rows come out in the order the ids list them.
+// ---------------------------------------------------------------------------
+constexpr int kEmitRegs = 32;  // 32 * 64 = 2048 ids per row at most
+
+__global__ __launch_bounds__(256) void emit_rows_kernel(
+    const int32_t* __restrict__ ids, int64_t rows, int32_t k, int32_t world, int32_t dcp_rank,
+    const int32_t* __restrict__ req_id, const int32_t* __restrict__ block_table, int64_t table_rows,
+    int32_t table_cols, int64_t ld_table, int32_t block_size, int64_t stride_rows,
+    int32_t* __restrict__ rows_out, int32_t out_cols, int32_t* __restrict__ valid_out) {
+    const int64_t row = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+    if (row >= rows) return;
+    const int lane = lane_id();
+    const int64_t req = req_id[row];
+    const bool req_ok = req >= 0 && req < table_rows;
+    const int32_t* idr = ids + row * (int64_t)k;
+    int32_t* outr = rows_out + row * (int64_t)out_cols;
+    const int32_t* bt = block_table + (req_ok ? req : 0) * ld_table;
+
+    int32_t g[kEmitRegs];
+#pragma unroll
+    for (int c = 0; c < kEmitRegs; ++c) {
+        const int j = c * kWave + lane;
+        g[c] = (req_ok && j < k) ? idr[j] : -1;
+    }
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int c = 0; c < kEmitRegs; ++c) {
+        if (c * kWave < k) {  // uniform
+            const int32_t gid = g[c];
+            const int32_t local = gid / world;
+            const int32_t b = local / block_size;
+            const bool own = gid >= 0 && gid - local * world == dcp_rank && b < table_cols;
+            const uint64_t m = __ballot(own);
+            if (own) {
+                const int64_t phys = (int64_t)bt[b] * stride_rows + (local - b * block_size);
+                outr[cnt + mbcnt64(m)] = (int32_t)(uint32_t)(uint64_t)phys;
+            }
+            cnt += (uint32_t)__popcll(m);
+        }
+    }
+    for (int32_t j = (int32_t)cnt + lane; j < out_cols; j += kWave) outr[j] = -1;
+    if (lane == 0) valid_out[row] = (int32_t)cnt;
+}
+
+// ---------------------------------------------------------------------------
 // Packed select, one wave per row, no barriers (world * ceil(n/64) <= 64).
 //
 // Lane l holds, for rank r and q = 0 .. qn-1, the word of slot j = q*64 + l in
@@ -1228,6 +1277,18 @@ int launch_merge_rescue(const int32_t* gathered, const int32_t* recv, int32_t wo
     const int rc = dispatch_kpt<RescueLaunch>(kpt, gathered, recv, world, rows, n, k, sat_word,
                                               out_ids, s);
     if (rc != RTS_OK) return rc;
+    return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
+}
+
+int launch_emit_rows(const int32_t* ids, int64_t rows, int32_t k, int32_t world, int32_t dcp_rank,
+                     const int32_t* req_id, const int32_t* block_table, int64_t table_rows,
+                     int32_t table_cols, int64_t ld_table, int32_t block_size, int64_t stride_rows,
+                     int32_t* rows_out, int32_t out_cols, int32_t* valid_out, hipStream_t s) {
+    if (rows == 0) return RTS_OK;
+    const int64_t blocks = (rows + 3) / 4;
+    hipLaunchKernelGGL(emit_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ids, rows, k, world,
+                       dcp_rank, req_id, block_table, table_rows, table_cols, ld_table, block_size,
+                       stride_rows, rows_out, out_cols, valid_out);
     return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
 }
 

@@ -390,3 +390,85 @@ def test_rescue_workload_pipeline_sampled(rts):
         for r in range(W):
             row[r::W] = vals[r, i]
         assert np.array_equal(np.sort(row[ids2[sample[i]]]), np.sort(row)[-K:]), sample[i]
+
+
+# ---------------------------------------------------------------------------
+# emit_rows: a rank's owned physical KV rows
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("world,block_size,k,out_cols", [
+    (8, 64, 2048, 2048), (8, 64, 512, 600), (3, 1, 37, 37), (1, 16, 64, 64), (16, 128, 1, 5),
+    (5, 7, 1000, 1024)])
+def test_emit_rows_random(rts, world, block_size, k, out_cols):
+    rng = np.random.default_rng(world * 17 + block_size + k)
+    rows, nreq, cols = 67, 9, 11
+    table = rng.integers(0, 1 << 21, size=(nreq, cols)).astype(np.int32)
+    table[1, :3] = 0x7FFFFFF0                      # wraps once scaled
+    req = rng.integers(-2, nreq + 2, size=rows).astype(np.int32)
+    ids = np.empty((rows, k), np.int32)
+    for t in range(rows):
+        ids[t] = rng.permutation(world * block_size * (cols + 3) + k)[:k]
+    ids[rng.random((rows, k)) < 0.1] = -1
+    stride = int(rng.integers(1, 1000))
+    ids_d, req_d, tab_d = dev(ids), dev(req), dev(table)
+    for rank in sorted({0, world - 1, world // 2}):
+        say("emit_rows", world, block_size, k, out_cols, rank)
+        rows_out = torch.full((rows, out_cols), 12345, dtype=torch.int32, device="cuda")
+        _, valid = rts.emit_rows(ids_d, world, rank, req_d, tab_d, block_size, stride,
+                                 rows_out=rows_out)
+        e_rows, e_valid = oracle.emit_rows(ids, world, rank, req, table, block_size, stride, out_cols)
+        assert_ids_equal(host(rows_out), e_rows, "rows_out")
+        assert np.array_equal(host(valid), e_valid), "valid_out"
+
+
+def test_emit_rows_strided_table(rts):
+    # A block table that is a column slice of a wider one (row stride > columns).
+    rng = np.random.default_rng(2)
+    world, B, k, rows = 4, 32, 256, 40
+    wide = rng.integers(0, 5000, size=(6, 20)).astype(np.int32)
+    req = rng.integers(0, 6, size=rows).astype(np.int32)
+    ids = np.stack([rng.permutation(world * B * 14)[:k] for _ in range(rows)]).astype(np.int32)
+    tab_d = dev(wide)[:, :12]
+    assert tab_d.stride(0) == 20
+    rows_out, valid = rts.emit_rows(dev(ids), world, 1, dev(req), tab_d, B, B)
+    e_rows, e_valid = oracle.emit_rows(ids, world, 1, req, wide[:, :12], B, B)
+    assert_ids_equal(host(rows_out), e_rows, "rows_out")
+    assert np.array_equal(host(valid), e_valid)
+
+
+def test_emit_rows_merge_workload(rts):
+    # Merge workload (6710 rows, 8 ranks, top-2048): every rank's owned rows of
+    # the GPU select; sampled rows against the oracle's emit_rows of the
+    # oracle's own select, and over all rows the ranks partition the ids.
+    W, R, N, K = datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_N, datagen.MERGE_K
+    B, nreq, cols = 64, 97, 300                   # local ids < 16384 need 256 blocks of 64
+    rng = np.random.default_rng(77)
+    table = np.stack([rng.permutation(200000)[:cols] for _ in range(nreq)]).astype(np.int32)
+    req = (np.arange(R) % nreq).astype(np.int32)
+    table_short = np.ascontiguousarray(table[:, :200])   # local ids past 200 * 64 drop out
+    say("emit_rows workload: generate")
+    ranks16 = datagen.bf16_bits(datagen.rank_slices(datagen.merge_global(), W))
+    x16 = bf16_dev(ranks16)
+    gathered = torch.empty((W, R, N + N // 32), dtype=torch.int32, device="cuda")
+    for r in range(W):
+        rts.pack_candidates(x16[r], rts.topk_rows(x16[r], N), out=gathered[r])
+    ids, _ = rts.merge_select_rank_major(gathered, K)
+    del x16
+    sample = np.arange(5, R, 97)
+    sub = ranks16[:, sample]
+    o_packed = np.stack([oracle.pack_candidates(sub[r], oracle.topk_rows(sub[r], None, N))
+                         for r in range(W)])
+    o_ids, _ = oracle.merge_select_rank_major(o_packed, K)
+    req_d = dev(req)
+    for tab in (table, table_short):
+        tab_d = dev(tab)
+        total = torch.zeros(R, dtype=torch.int64, device="cuda")
+        for rank in range(W):
+            say("emit_rows workload rank", rank, tab.shape)
+            rows_out, valid = rts.emit_rows(ids, W, rank, req_d, tab_d, B, B)
+            total += valid.long()
+            e_rows, e_valid = oracle.emit_rows(o_ids, W, rank, req[sample], tab, B, B)
+            assert_ids_equal(host(rows_out)[sample], e_rows, "rows_out")
+            assert np.array_equal(host(valid)[sample], e_valid)
+        inside = (((ids // W) // B) < tab.shape[1]).sum(dim=1)
+        assert torch.equal(total, inside.long()), "ranks do not partition the selected ids"
