@@ -174,9 +174,15 @@ def secondary(torch, rts, datagen, steps, warmup):
     _, t_emit = time_calls(lambda: rts.emit_rows(ids, W, 3, req, table, 64, 64, rows_out=rows_out,
                                                  valid_out=valid), steps, warmup, torch)
     emit_bytes = R * K * 4 * 2 + R * 8
+    # The same rows straight from the select (no ids written or re-read).
+    _, t_fused = time_calls(lambda: rts.merge_select_rank_major_rows(gathered, K, 3, req, table, 64, 64,
+                                                                     rows_out=rows_out, valid_out=valid),
+                            steps, warmup, torch)
     res["emit_rows"] = {"shape": [R, K], "world": W, "block_size": 64, "us_per_call": t_emit * 1e6,
                         "owned_rows_per_row": float(valid.float().mean()),
-                        "algorithmic_GBps": emit_bytes / t_emit / 1e9}
+                        "algorithmic_GBps": emit_bytes / t_emit / 1e9,
+                        "select_plus_emit_rows_us": (t_sel + t_emit) * 1e6,
+                        "fused_select_rows_us": t_fused * 1e6}
     del rows_out, valid
     res["merge_packed"] = {"shape": [W, R, N + N // 32], "k": K,
                            "select_us": t_sel * 1e6, "select_rows_per_s": R / t_sel,

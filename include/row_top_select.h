@@ -222,6 +222,50 @@ int emit_rows(const int32_t* ids, int64_t rows, int32_t k, int32_t world, int32_
               int32_t out_cols, int32_t* valid_out, hipStream_t stream);
 
 /*
+ * rts_kv_rows -- where the fused selects below write this rank's owned
+ * physical KV rows; the fields mean what the arguments of emit_rows of the
+ * same names mean (all pointers device pointers, owned by the caller).
+ */
+typedef struct {
+    int32_t dcp_rank;           /* 0 <= dcp_rank < world */
+    const int32_t* req_id;      /* [rows] */
+    const int32_t* block_table; /* [table_rows, ld_table], first table_cols columns used */
+    int64_t table_rows;
+    int32_t table_cols;
+    int64_t ld_table;           /* >= table_cols */
+    int32_t block_size;         /* >= 1 */
+    int64_t stride_rows;
+    int32_t* rows_out;          /* [rows, out_cols], contiguous, out_cols >= k */
+    int32_t out_cols;
+    int32_t* valid_out;         /* [rows] */
+} rts_kv_rows;
+
+/*
+ * merge_select_rank_major_rows -- merge_select_rank_major that writes this
+ * rank's owned physical rows straight from the select ([P2]
+ * DCPTopkSelectKernel docstring: emit_ids and/or emit_rows;
+ * dcp_topk_merge_rows).  For the same words, kv->rows_out and kv->valid_out
+ * are exactly what emit_rows writes for the ids merge_select_rank_major
+ * returns, and out_ids (optional, NULL = not written) and sat_word (NULL =
+ * not written) are what merge_select_rank_major writes.
+ * Errors: those of merge_select_rank_major; RTS_EINVAL for an invalid kv.
+ */
+int merge_select_rank_major_rows(const int32_t* gathered, int32_t world, int64_t rows, int32_t n,
+                                 int32_t k, const rts_kv_rows* kv, int32_t* out_ids, int32_t* sat_word,
+                                 hipStream_t stream);
+
+/*
+ * merge_rescue_rank_major_rows -- merge_rescue_rank_major that also (or
+ * only: out_ids may be NULL) rewrites kv->rows_out and kv->valid_out of the
+ * rows that enter the second round, as emit_rows would for their new ids.
+ * Rows that do not enter are not written.
+ * Errors: those of merge_rescue_rank_major; RTS_EINVAL for an invalid kv.
+ */
+int merge_rescue_rank_major_rows(const int32_t* gathered, const int32_t* recv, int32_t world,
+                                 int64_t rows, int32_t n, int32_t k, const int32_t* sat_word,
+                                 const rts_kv_rows* kv, int32_t* out_ids, hipStream_t stream);
+
+/*
  * pack_pairs -- a rank's local top-kc as (score, global id) pairs ([P1]
  * Overview: "pack(local_topk)" into [R, K, 2]).
  *

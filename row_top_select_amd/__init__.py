@@ -40,12 +40,25 @@ _lib.merge_select_row_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p, _p]
 _lib.merge_select_pairs_row_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p]
 _lib.emit_rows.argtypes = [_p, _i64, _i32, _i32, _i32, _p, _p, _i64, _i32, _i64, _i32, _i64, _p, _i32,
                            _p, _p]
+_lib.merge_select_rank_major_rows.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p, _p, _p]
+_lib.merge_rescue_rank_major_rows.argtypes = [_p, _p, _i32, _i64, _i32, _i32, _p, _p, _p, _p]
 _lib.rescue_push.argtypes = [_p, _i32, _i32, _i64, _i32, _i32, _p, _p, _p]
 _lib.merge_rescue_rank_major.argtypes = [_p, _p, _i32, _i64, _i32, _i32, _p, _p, _p]
 for _f in (_lib.topk_rows, _lib.pack_candidates, _lib.merge_select_rank_major, _lib.pack_pairs,
            _lib.merge_select_pairs_rank_major, _lib.rescue_push, _lib.merge_rescue_rank_major,
-           _lib.merge_select_row_major, _lib.merge_select_pairs_row_major, _lib.emit_rows):
+           _lib.merge_select_row_major, _lib.merge_select_pairs_row_major, _lib.emit_rows,
+           _lib.merge_select_rank_major_rows, _lib.merge_rescue_rank_major_rows):
     _f.restype = ctypes.c_int
+
+
+class _KvRows(ctypes.Structure):
+    """rts_kv_rows of include/row_top_select.h."""
+    _fields_ = [("dcp_rank", ctypes.c_int32), ("req_id", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("table_rows", ctypes.c_int64),
+                ("table_cols", ctypes.c_int32), ("ld_table", ctypes.c_int64),
+                ("block_size", ctypes.c_int32), ("stride_rows", ctypes.c_int64),
+                ("rows_out", ctypes.c_void_p), ("out_cols", ctypes.c_int32),
+                ("valid_out", ctypes.c_void_p)]
 
 
 class RtsError(RuntimeError):
@@ -302,6 +315,81 @@ def emit_rows(ids: torch.Tensor, world: int, dcp_rank: int, req_id: torch.Tensor
                           _dev(block_table, "block_table"), table_rows, table_cols, ld_table,
                           block_size, stride_rows, _dev(rows_out, "rows_out"), rows_out.shape[1],
                           _dev(valid_out, "valid_out"), _stream(stream)), "emit_rows")
+    return rows_out, valid_out
+
+
+def _kv_rows(rows, k, dcp_rank, req_id, block_table, block_size, stride_rows, rows_out, valid_out,
+             device):
+    req_id = _int32_vec(req_id, rows, "req_id")
+    if req_id is None:
+        raise ValueError("req_id is required")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+            (block_table.shape[1] > 1 and block_table.stride(1) != 1):
+        raise ValueError("block_table must be int32 [Q, B_max] with unit column stride")
+    table_rows, table_cols = block_table.shape
+    ld_table = block_table.stride(0) if table_rows > 1 else table_cols
+    if rows_out is None:
+        rows_out = torch.empty((rows, k), dtype=torch.int32, device=device)
+    if rows_out.dtype != torch.int32 or rows_out.dim() != 2 or rows_out.shape[0] != rows or \
+            rows_out.shape[1] < k or not rows_out.is_contiguous():
+        raise ValueError(f"rows_out must be contiguous int32 [{rows}, >= {k}]")
+    if valid_out is None:
+        valid_out = torch.empty((rows,), dtype=torch.int32, device=device)
+    valid_out = _int32_vec(valid_out, rows, "valid_out")
+    kv = _KvRows(dcp_rank, req_id.data_ptr(), block_table.data_ptr(), table_rows, table_cols, ld_table,
+                 block_size, stride_rows, rows_out.data_ptr(), rows_out.shape[1], valid_out.data_ptr())
+    return kv, rows_out, valid_out
+
+
+def merge_select_rank_major_rows(gathered: torch.Tensor, k: int, dcp_rank: int, req_id: torch.Tensor,
+                                 block_table: torch.Tensor, block_size: int, stride_rows: int,
+                                 rows_out: torch.Tensor | None = None,
+                                 valid_out: torch.Tensor | None = None,
+                                 out_ids: torch.Tensor | None = None,
+                                 sat_word: torch.Tensor | None = None, stream=None):
+    """Packed select writing this rank's owned physical rows (and optionally
+    ids / sat_word); returns (rows_out, valid_out, out_ids, sat_word)."""
+    if gathered.dtype != torch.int32 or gathered.dim() != 3 or not gathered.is_contiguous():
+        raise ValueError("gathered must be contiguous int32 [W, R, n + n/32]")
+    world, rows, _ = gathered.shape
+    n = _packed_width(gathered, "gathered")
+    kv, rows_out, valid_out = _kv_rows(rows, k, dcp_rank, req_id, block_table, block_size, stride_rows,
+                                       rows_out, valid_out, gathered.device)
+    if out_ids is not None and (out_ids.dtype != torch.int32 or tuple(out_ids.shape) != (rows, k) or
+                                not out_ids.is_contiguous()):
+        raise ValueError(f"out_ids must be contiguous int32 [{rows}, {k}]")
+    sat_word = _int32_vec(sat_word, rows, "sat_word")
+    _check(_lib.merge_select_rank_major_rows(_dev(gathered, "gathered"), world, rows, n, k,
+                                             ctypes.byref(kv), _opt(out_ids, "out_ids"),
+                                             _opt(sat_word, "sat_word"), _stream(stream)),
+           "merge_select_rank_major_rows")
+    return rows_out, valid_out, out_ids, sat_word
+
+
+def merge_rescue_rank_major_rows(gathered: torch.Tensor, recv: torch.Tensor, sat_word: torch.Tensor,
+                                 k: int, dcp_rank: int, req_id: torch.Tensor,
+                                 block_table: torch.Tensor, block_size: int, stride_rows: int,
+                                 rows_out: torch.Tensor, valid_out: torch.Tensor,
+                                 out_ids: torch.Tensor | None = None, stream=None):
+    """Second round rewriting the owned rows (and optionally ids) of the rows
+    that enter it, in place; returns (rows_out, valid_out)."""
+    if gathered.dtype != torch.int32 or gathered.dim() != 3 or not gathered.is_contiguous():
+        raise ValueError("gathered must be contiguous int32 [W, R, n + n/32]")
+    world, rows, _ = gathered.shape
+    n = _packed_width(gathered, "gathered")
+    kv, rows_out, valid_out = _kv_rows(rows, k, dcp_rank, req_id, block_table, block_size, stride_rows,
+                                       rows_out, valid_out, gathered.device)
+    sat_word = _int32_vec(sat_word, rows, "sat_word")
+    if (recv.dtype != torch.int32 or not recv.is_contiguous() or
+            tuple(recv.shape) != (rows, rescue_slots(n, k), k + k // 32)):
+        raise ValueError(f"recv must be contiguous int32 [{rows}, {rescue_slots(n, k)}, {k + k // 32}]")
+    if out_ids is not None and (out_ids.dtype != torch.int32 or tuple(out_ids.shape) != (rows, k) or
+                                not out_ids.is_contiguous()):
+        raise ValueError(f"out_ids must be contiguous int32 [{rows}, {k}]")
+    _check(_lib.merge_rescue_rank_major_rows(_dev(gathered, "gathered"), _dev(recv, "recv"), world, rows,
+                                             n, k, _dev(sat_word, "sat_word"), ctypes.byref(kv),
+                                             _opt(out_ids, "out_ids"), _stream(stream)),
+           "merge_rescue_rank_major_rows")
     return rows_out, valid_out
 
 

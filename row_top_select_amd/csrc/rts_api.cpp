@@ -84,7 +84,8 @@ int merge_packed_checked(const int32_t* gathered, bool row_major, int32_t world,
     if (!gathered || !out_ids) return RTS_EINVAL;
     if (!aligned(gathered, 4) || !aligned(out_ids, 4) || (sat_word && !aligned(sat_word, 4)))
         return RTS_EINVAL;
-    return rts::launch_merge_packed(gathered, row_major, world, rows, n, k, out_ids, sat_word, stream);
+    return rts::launch_merge_packed(gathered, row_major, world, rows, n, k, out_ids, sat_word, nullptr,
+                                    stream);
 }
 
 int merge_pairs_checked(const int32_t* gathered_pairs, bool row_major, int32_t world, int64_t rows,
@@ -131,7 +132,7 @@ int merge_rescue_rank_major(const int32_t* gathered, const int32_t* recv, int32_
     if (!gathered || !recv || !sat_word || !out_ids) return RTS_EINVAL;
     if (!aligned(gathered, 4) || !aligned(recv, 4) || !aligned(sat_word, 4) || !aligned(out_ids, 4))
         return RTS_EINVAL;
-    return rts::launch_merge_rescue(gathered, recv, world, rows, n, k, sat_word, out_ids, stream);
+    return rts::launch_merge_rescue(gathered, recv, world, rows, n, k, sat_word, out_ids, nullptr, stream);
 }
 
 int emit_rows(const int32_t* ids, int64_t rows, int32_t k, int32_t world, int32_t dcp_rank,
@@ -151,6 +152,58 @@ int emit_rows(const int32_t* ids, int64_t rows, int32_t k, int32_t world, int32_
     return rts::launch_emit_rows(ids, rows, k, world, dcp_rank, req_id, block_table, table_rows,
                                  table_cols, ld_table, block_size, stride_rows, rows_out, out_cols,
                                  valid_out, stream);
+}
+
+namespace {
+// Validates an rts_kv_rows against k and world and converts it.
+int kv_rows_args(const rts_kv_rows* kv, int32_t k, int32_t world, rts::RowsArgs& ra) {
+    if (!kv || kv->dcp_rank < 0 || kv->dcp_rank >= world || kv->table_rows < 0 || kv->table_cols < 0 ||
+        kv->ld_table < kv->table_cols || kv->block_size < 1 || kv->out_cols < k)
+        return RTS_EINVAL;
+    if (!kv->req_id || !kv->rows_out || !kv->valid_out ||
+        (kv->table_rows > 0 && kv->table_cols > 0 && !kv->block_table))
+        return RTS_EINVAL;
+    if (!aligned(kv->req_id, 4) || !aligned(kv->rows_out, 4) || !aligned(kv->valid_out, 4) ||
+        (kv->block_table && !aligned(kv->block_table, 4)))
+        return RTS_EINVAL;
+    ra = rts::RowsArgs{kv->req_id, kv->block_table, kv->rows_out, kv->valid_out, kv->table_rows,
+                       kv->ld_table, kv->stride_rows, kv->dcp_rank, kv->table_cols, kv->block_size,
+                       kv->out_cols};
+    return RTS_OK;
+}
+}  // namespace
+
+int merge_select_rank_major_rows(const int32_t* gathered, int32_t world, int64_t rows, int32_t n,
+                                 int32_t k, const rts_kv_rows* kv, int32_t* out_ids, int32_t* sat_word,
+                                 hipStream_t stream) {
+    if (world < 1 || world > 16 || rows < 0 || n < 32 || n % 32 != 0 || k < 1) return RTS_EINVAL;
+    if (k > kMaxK || (int64_t)world * n > kMaxCandidates || rows > kMaxGrid) return RTS_EUNSUPPORTED;
+    rts::RowsArgs ra;
+    const int rc = kv_rows_args(kv, k, world, ra);
+    if (rc != RTS_OK) return rc;
+    if (rows == 0) return RTS_OK;
+    if (!gathered || !aligned(gathered, 4) || (out_ids && !aligned(out_ids, 4)) ||
+        (sat_word && !aligned(sat_word, 4)))
+        return RTS_EINVAL;
+    return rts::launch_merge_packed(gathered, false, world, rows, n, k, out_ids, sat_word, &ra, stream);
+}
+
+int merge_rescue_rank_major_rows(const int32_t* gathered, const int32_t* recv, int32_t world,
+                                 int64_t rows, int32_t n, int32_t k, const int32_t* sat_word,
+                                 const rts_kv_rows* kv, int32_t* out_ids, hipStream_t stream) {
+    if (world < 1 || world > 16 || rows < 0 || n < 32 || n % 32 != 0 || k < 32 || k % 32 != 0)
+        return RTS_EINVAL;
+    if (k > kMaxK || rts::rescue_candidates(world, n, k) > kMaxCandidates || rows > kMaxGrid)
+        return RTS_EUNSUPPORTED;
+    rts::RowsArgs ra;
+    const int rc = kv_rows_args(kv, k, world, ra);
+    if (rc != RTS_OK) return rc;
+    if (rows == 0 || (k - 1) / n == 0) return RTS_OK;
+    if (!gathered || !recv || !sat_word) return RTS_EINVAL;
+    if (!aligned(gathered, 4) || !aligned(recv, 4) || !aligned(sat_word, 4) ||
+        (out_ids && !aligned(out_ids, 4)))
+        return RTS_EINVAL;
+    return rts::launch_merge_rescue(gathered, recv, world, rows, n, k, sat_word, out_ids, &ra, stream);
 }
 
 int pack_pairs(const float* logits, int64_t rows, int64_t cols, int64_t ld_logits,

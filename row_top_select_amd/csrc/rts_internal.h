@@ -8,6 +8,18 @@
 
 namespace rts {
 
+// A rank's owned physical KV rows, emitted by a packed select next to (or
+// instead of) the global ids (kernels page: DCPTopkSelectKernel docstring on
+// emit_rows, dcp_topk_merge_rows).  rows_out == nullptr: not requested.
+struct RowsArgs {
+    const int32_t* req_id;       // [rows]
+    const int32_t* block_table;  // [table_rows, ld_table]
+    int32_t* rows_out;           // [rows, out_cols]
+    int32_t* valid_out;          // [rows]
+    int64_t table_rows, ld_table, stride_rows;
+    int32_t dcp_rank, table_cols, block_size, out_cols;
+};
+
 // Launch geometry of topk_rows for one problem shape.
 struct TopkPlan {
     int e;          // sorted-list length per lane (list = 64 * e >= k)
@@ -34,7 +46,7 @@ int launch_pack_pairs(const float* x, int64_t rows, int64_t cols, int64_t ld,
 // row_major: gathered is [rows, world, n + n/32] instead of [world, rows, n + n/32].
 int launch_merge_packed(const int32_t* gathered, bool row_major, int32_t world, int64_t rows,
                         int32_t n, int32_t k, int32_t* out_ids, int32_t* sat_word,
-                        hipStream_t stream);
+                        const RowsArgs* rows_args, hipStream_t stream);
 
 // Candidate slots of one rescued row: world * n round-1 words plus k words
 // for each of at most min((k-1)/n, world) receive slots.
@@ -46,7 +58,7 @@ int launch_rescue_push(const int32_t* local_packed, int32_t rank, int32_t world,
 
 int launch_merge_rescue(const int32_t* gathered, const int32_t* recv, int32_t world, int64_t rows,
                         int32_t n, int32_t k, const int32_t* sat_word, int32_t* out_ids,
-                        hipStream_t stream);
+                        const RowsArgs* rows_args, hipStream_t stream);
 
 int launch_emit_rows(const int32_t* ids, int64_t rows, int32_t k, int32_t world, int32_t dcp_rank,
                      const int32_t* req_id, const int32_t* block_table, int64_t table_rows,

@@ -44,6 +44,23 @@ struct Layout {
     __host__ __device__ int64_t at(int64_t r, int64_t row) const { return r * rank_stride + row * row_stride; }
 };
 
+// The block-table row of `row` (nullptr: the request is outside the table,
+// so the row owns nothing).
+__device__ __forceinline__ const int32_t* rows_table_of(const RowsArgs& ra, int64_t row) {
+    const int64_t req = ra.req_id[row];
+    return (req >= 0 && req < ra.table_rows) ? ra.block_table + req * ra.ld_table : nullptr;
+}
+
+// Physical row of local index `local` when its KV block is inside the table.
+__device__ __forceinline__ bool owned_phys(const RowsArgs& ra, const int32_t* bt, uint32_t local,
+                                           int32_t& phys) {
+    const uint32_t b = local / (uint32_t)ra.block_size;
+    if (bt == nullptr || b >= (uint32_t)ra.table_cols) return false;
+    const int64_t v = (int64_t)bt[b] * ra.stride_rows + (int64_t)(local - b * (uint32_t)ra.block_size);
+    phys = (int32_t)(uint32_t)(uint64_t)v;
+    return true;
+}
+
 struct SelectSmem {
     uint32_t hist[kHistCopies][kHistStride];
     uint32_t bins[256];
@@ -210,6 +227,49 @@ __device__ void block_emit(const uint64_t (&key)[KPT], uint64_t T, int k, int32_
     for (int p = filled + t; p < k; p += kSelBlock) out[p] = -1;
 }
 
+// The owned physical rows of the keys >= T (gid = composite id; owned iff
+// gid % world == dcp_rank), in the same flat order as block_emit, then -1 up
+// to out_cols, and their count.
+template <int KPT>
+__device__ void block_emit_rows(const uint64_t (&key)[KPT], uint64_t T, int32_t world, int64_t row,
+                                const RowsArgs& ra, SelectSmem& sm) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    __syncthreads();  // block_emit may still be reading sm.tab
+    const int32_t* bt = rows_table_of(ra, row);
+    uint64_t m[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const uint32_t gid = composite_id(key[i]);
+        const uint32_t local = gid / (uint32_t)world;
+        int32_t phys;
+        const bool own = key[i] != 0ull && key[i] >= T && gid - local * (uint32_t)world == (uint32_t)ra.dcp_rank &&
+                         owned_phys(ra, bt, local, phys);
+        m[i] = __ballot(own);
+        if (lane == 0) sm.tab[i * kSelWaves + wave] = (uint32_t)__popcll(m[i]);
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    const uint32_t v = t < KPT * kSelWaves ? sm.tab[t] : 0u;
+    uint32_t excl;
+    const uint32_t total = block_excl_scan(v, excl, sm);
+    if (t < KPT * kSelWaves) sm.tab[t] = excl;
+    __syncthreads();
+    int32_t* orow = ra.rows_out + row * (int64_t)ra.out_cols;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        if ((m[i] >> lane) & 1ull) {
+            const uint32_t gid = composite_id(key[i]);
+            const uint32_t local = gid / (uint32_t)world;
+            int32_t phys = -1;
+            owned_phys(ra, bt, local, phys);
+            orow[sm.tab[i * kSelWaves + wave] + mbcnt64(m[i])] = phys;
+        }
+    }
+    for (int p = (int)total + t; p < ra.out_cols; p += kSelBlock) orow[p] = -1;
+    if (t == 0) ra.valid_out[row] = (int32_t)total;
+    __syncthreads();  // sm.tab is reused by the caller
+}
+
 // ---------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------
@@ -292,10 +352,10 @@ struct FlatWalk {
     }
 };
 
-template <int KPT>
+template <int KPT, bool ROWS>
 __global__ __launch_bounds__(kSelBlock) void merge_packed_kernel(
     const int32_t* __restrict__ gathered, Layout lay, int32_t world, int64_t rows, int32_t n,
-    int32_t k, int32_t* __restrict__ out_ids, int32_t* __restrict__ sat_word) {
+    int32_t k, int32_t* __restrict__ out_ids, int32_t* __restrict__ sat_word, RowsArgs ra) {
     __shared__ SelectSmem sm;
     const int t = threadIdx.x, lane = lane_id();
     const int64_t row = blockIdx.x;
@@ -333,7 +393,8 @@ __global__ __launch_bounds__(kSelBlock) void merge_packed_kernel(
 
     uint64_t T = 1ull;
     if (nvalid > (uint32_t)k) T = block_radix_kth<KPT>(key, k, sm);
-    block_emit<KPT>(key, T, k, out_ids + row * (int64_t)k, sm);
+    if (out_ids) block_emit<KPT>(key, T, k, out_ids + row * (int64_t)k, sm);
+    if constexpr (ROWS) block_emit_rows<KPT>(key, T, world, row, ra, sm);
 
     if (sat_word) {
         // tau16: ord16 of the k-th selected composite (the smallest selected).
@@ -406,12 +467,12 @@ __global__ __launch_bounds__(256) void rescue_push_kernel(
 // (s, j) = ((f - world*n) / k, (f - world*n) % k), owned by the s-th set bit
 // of the mask.  Selection and emission in flat order are the round-1 block
 // kernel's.
-template <int KPT, bool IN_LOOP>
+template <int KPT, bool IN_LOOP, bool ROWS>
 __device__ __forceinline__ void rescue_one_row(const int32_t* __restrict__ gathered,
                                                const int32_t* __restrict__ recv, int32_t world,
                                                int64_t rows, int32_t n, int32_t k, int64_t row,
                                                uint32_t sw, int32_t* __restrict__ out_ids,
-                                               SelectSmem& sm) {
+                                               const RowsArgs& ra, SelectSmem& sm) {
     // Inside a row loop, an opaque copy of the thread index renewed per row:
     // without it the compiler hoists the per-register slot arithmetic out of
     // the loop and keeps all of it live across rows.
@@ -463,22 +524,23 @@ __device__ __forceinline__ void rescue_one_row(const int32_t* __restrict__ gathe
 
     uint64_t T = 1ull;
     if (nvalid > (uint32_t)k) T = block_radix_kth<KPT>(key, k, sm);
-    block_emit<KPT>(key, T, k, out_ids + row * (int64_t)k, sm);
+    if (out_ids) block_emit<KPT>(key, T, k, out_ids + row * (int64_t)k, sm);
+    if constexpr (ROWS) block_emit_rows<KPT>(key, T, world, row, ra, sm);
     if constexpr (IN_LOOP) __syncthreads();  // block_emit's table is reused by the next row
 }
 
 // One workgroup per row (grid = rows); a row that does not enter returns at once.
-template <int KPT>
+template <int KPT, bool ROWS>
 __global__ __launch_bounds__(kSelBlock) void merge_rescue_row_kernel(
     const int32_t* __restrict__ gathered, const int32_t* __restrict__ recv, int32_t world,
     int64_t rows, int32_t n, int32_t k, const int32_t* __restrict__ sat_word,
-    int32_t* __restrict__ out_ids) {
+    int32_t* __restrict__ out_ids, RowsArgs ra) {
     __shared__ SelectSmem sm;
     const int64_t row = blockIdx.x;
     const uint32_t sw = (uint32_t)sat_word[row];
     if (!rescue_row(sw, world, (k - 1) / n)) return;
     for (int q = threadIdx.x; q < kHistCopies * kHistStride; q += kSelBlock) (&sm.hist[0][0])[q] = 0u;
-    rescue_one_row<KPT, false>(gathered, recv, world, rows, n, k, row, sw, out_ids, sm);
+    rescue_one_row<KPT, false, ROWS>(gathered, recv, world, rows, n, k, row, sw, out_ids, ra, sm);
 }
 
 // Rows dealt to workgroups with stride gridDim.x.  A workgroup reads the
@@ -486,11 +548,12 @@ __global__ __launch_bounds__(kSelBlock) void merge_rescue_row_kernel(
 // those that enter the second round in LDS, then selects them one by one, so
 // a row that does not enter costs one word load and no workgroup launch.
 // Held to 4 waves per SIMD (two workgroups per compute unit).
-template <int KPT>
+template <int KPT, bool ROWS>
 __global__ __launch_bounds__(kSelBlock) __attribute__((amdgpu_waves_per_eu(4)))
 void merge_rescue_kernel(const int32_t* __restrict__ gathered, const int32_t* __restrict__ recv,
                          int32_t world, int64_t rows, int32_t n, int32_t k,
-                         const int32_t* __restrict__ sat_word, int32_t* __restrict__ out_ids) {
+                         const int32_t* __restrict__ sat_word, int32_t* __restrict__ out_ids,
+                         RowsArgs ra) {
     __shared__ SelectSmem sm;
     __shared__ uint32_t todo[kSelBlock];
     __shared__ uint32_t todo_sw[kSelBlock];
@@ -522,7 +585,8 @@ void merge_rescue_kernel(const int32_t* __restrict__ gathered, const int32_t* __
         }
         for (uint32_t q = 0; q < cnt; ++q) {
             const int64_t row = base + (int64_t)todo[q] * gridDim.x;
-            rescue_one_row<KPT, true>(gathered, recv, world, rows, n, k, row, todo_sw[q], out_ids, sm);
+            rescue_one_row<KPT, true, ROWS>(gathered, recv, world, rows, n, k, row, todo_sw[q], out_ids,
+                                            ra, sm);
         }
     }
 }
@@ -598,10 +662,10 @@ __device__ __forceinline__ uint32_t packed_gid(uint32_t word, uint32_t hibit, ui
     return local * world + r;
 }
 
-template <int QN, int W>
+template <int QN, int W, bool ROWS>
 __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
     const int32_t* __restrict__ gathered, Layout lay, int32_t world_, int64_t rows, int32_t n,
-    int32_t k, int32_t* __restrict__ out_ids, int32_t* __restrict__ sat_word) {
+    int32_t k, int32_t* __restrict__ out_ids, int32_t* __restrict__ sat_word, RowsArgs ra) {
     constexpr int NR = QN * W;  // registers: rank r = i / QN, q = i % QN
     constexpr int32_t world = W;
     (void)world_;
@@ -781,9 +845,13 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
     if (nz <= (uint32_t)k) thr_gt = 0u;  // every nonzero word is selected
 
     // Emission in candidate order; saturation: rank r keeps its bit iff all n
-    // of its words are nonzero with a score above tau16.
-    int32_t* o_row = out_ids + row * (int64_t)k;
-    int base = 0;
+    // of its words are nonzero with a score above tau16.  Owned physical rows
+    // (when requested) are the selected words of rank dcp_rank, in the same order.
+    int32_t* o_row = out_ids ? out_ids + row * (int64_t)k : nullptr;
+    constexpr bool want_rows = ROWS;
+    const int32_t* bt = want_rows ? rows_table_of(ra, row) : nullptr;
+    int32_t* r_row = want_rows ? ra.rows_out + row * (int64_t)ra.out_cols : nullptr;
+    int base = 0, rbase = 0;
     uint32_t notsat = 0u;
     fresh();
 #pragma unroll
@@ -797,13 +865,26 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
             const bool sel = w[i] != 0u && (o > thr_gt || (o == tie16 && gid <= gid_cut));
             const uint64_t m = __ballot(sel);
             const int pos = base + (int)mbcnt64(m);
-            if (sel && pos < k) o_row[pos] = (int32_t)gid;
+            if (o_row && sel && pos < k) o_row[pos] = (int32_t)gid;
             base += (int)__popcll(m);
             bad |= __ballot((q < QN - 1 || q * kWave + lane < n) && (w[i] == 0u || o <= tau16));
+            if (want_rows && r == ra.dcp_rank) {  // uniform
+                int32_t phys = -1;
+                const bool own = sel && owned_phys(ra, bt, gid / (uint32_t)world, phys);
+                const uint64_t om = __ballot(own);
+                const int rp = rbase + (int)mbcnt64(om);
+                if (own && rp < ra.out_cols) r_row[rp] = phys;
+                rbase += (int)__popcll(om);
+            }
         }
         if (bad) notsat |= 1u << r;
     }
-    for (int p = (base < k ? base : k) + lane; p < k; p += kWave) o_row[p] = -1;
+    if (o_row)
+        for (int p = (base < k ? base : k) + lane; p < k; p += kWave) o_row[p] = -1;
+    if (want_rows) {
+        for (int p = rbase + lane; p < ra.out_cols; p += kWave) r_row[p] = -1;
+        if (lane == 0) ra.valid_out[row] = rbase;
+    }
     if (sat_word && lane == 0) {
         uint32_t mask = ~notsat & ((1u << world) - 1u);
         if (__popc(mask) > (k - 1) / n) mask = 0u;
@@ -1145,9 +1226,13 @@ int dispatch_kpt(int kpt, A... args) {
 template <int KPT>
 struct PackedLaunch {
     static void run(const int32_t* g, Layout lay, int32_t world, int64_t rows, int32_t n, int32_t k,
-                    int32_t* ids, int32_t* sat, hipStream_t s) {
-        hipLaunchKernelGGL((merge_packed_kernel<KPT>), dim3((unsigned)rows), dim3(kSelBlock), 0, s, g,
-                           lay, world, rows, n, k, ids, sat);
+                    int32_t* ids, int32_t* sat, RowsArgs ra, hipStream_t s) {
+        if (ra.rows_out)
+            hipLaunchKernelGGL((merge_packed_kernel<KPT, true>), dim3((unsigned)rows), dim3(kSelBlock), 0,
+                               s, g, lay, world, rows, n, k, ids, sat, ra);
+        else
+            hipLaunchKernelGGL((merge_packed_kernel<KPT, false>), dim3((unsigned)rows), dim3(kSelBlock), 0,
+                               s, g, lay, world, rows, n, k, ids, sat, ra);
     }
 };
 
@@ -1157,14 +1242,22 @@ constexpr int64_t kRescueGrid = 512;
 template <int KPT>
 struct RescueLaunch {
     static void run(const int32_t* g, const int32_t* recv, int32_t world, int64_t rows, int32_t n,
-                    int32_t k, const int32_t* sat, int32_t* ids, hipStream_t s) {
+                    int32_t k, const int32_t* sat, int32_t* ids, RowsArgs ra, hipStream_t s) {
+        if (ra.rows_out)
+            go<true>(g, recv, world, rows, n, k, sat, ids, ra, s);
+        else
+            go<false>(g, recv, world, rows, n, k, sat, ids, ra, s);
+    }
+    template <bool ROWS>
+    static void go(const int32_t* g, const int32_t* recv, int32_t world, int64_t rows, int32_t n,
+                   int32_t k, const int32_t* sat, int32_t* ids, RowsArgs ra, hipStream_t s) {
         if constexpr (KPT >= 48) {
-            hipLaunchKernelGGL((merge_rescue_row_kernel<KPT>), dim3((unsigned)rows), dim3(kSelBlock), 0,
-                               s, g, recv, world, rows, n, k, sat, ids);
+            hipLaunchKernelGGL((merge_rescue_row_kernel<KPT, ROWS>), dim3((unsigned)rows), dim3(kSelBlock),
+                               0, s, g, recv, world, rows, n, k, sat, ids, ra);
         } else {
             const unsigned grid = (unsigned)(rows < kRescueGrid ? rows : kRescueGrid);
-            hipLaunchKernelGGL((merge_rescue_kernel<KPT>), dim3(grid), dim3(kSelBlock), 0, s, g, recv,
-                               world, rows, n, k, sat, ids);
+            hipLaunchKernelGGL((merge_rescue_kernel<KPT, ROWS>), dim3(grid), dim3(kSelBlock), 0, s, g,
+                               recv, world, rows, n, k, sat, ids, ra);
         }
     }
 };
@@ -1180,22 +1273,27 @@ struct PairsLaunch {
 
 template <int QN, int W>
 void launch_packed_wave(const int32_t* g, Layout lay, int64_t rows, int32_t n, int32_t k,
-                        int32_t* ids, int32_t* sat, hipStream_t s) {
-    if constexpr (QN * W <= 64)
-        hipLaunchKernelGGL((merge_packed_wave_kernel<QN, W>), dim3((unsigned)rows), dim3(kWave), 0,
-                           s, g, lay, W, rows, n, k, ids, sat);
+                        int32_t* ids, int32_t* sat, const RowsArgs& ra, hipStream_t s) {
+    if constexpr (QN * W <= 64) {
+        if (ra.rows_out)
+            hipLaunchKernelGGL((merge_packed_wave_kernel<QN, W, true>), dim3((unsigned)rows), dim3(kWave),
+                               0, s, g, lay, W, rows, n, k, ids, sat, ra);
+        else
+            hipLaunchKernelGGL((merge_packed_wave_kernel<QN, W, false>), dim3((unsigned)rows), dim3(kWave),
+                               0, s, g, lay, W, rows, n, k, ids, sat, ra);
+    }
 }
 
 template <int QN>
 bool packed_wave_w(int world, const int32_t* g, Layout lay, int64_t rows, int32_t n, int32_t k,
-                   int32_t* ids, int32_t* sat, hipStream_t s) {
+                   int32_t* ids, int32_t* sat, const RowsArgs& ra, hipStream_t s) {
     if (QN * world > 64) return false;
     switch (world) {
-        case 1: launch_packed_wave<QN, 1>(g, lay, rows, n, k, ids, sat, s); return true;
-        case 2: launch_packed_wave<QN, 2>(g, lay, rows, n, k, ids, sat, s); return true;
-        case 4: launch_packed_wave<QN, 4>(g, lay, rows, n, k, ids, sat, s); return true;
-        case 8: launch_packed_wave<QN, 8>(g, lay, rows, n, k, ids, sat, s); return true;
-        case 16: launch_packed_wave<QN, 16>(g, lay, rows, n, k, ids, sat, s); return true;
+        case 1: launch_packed_wave<QN, 1>(g, lay, rows, n, k, ids, sat, ra, s); return true;
+        case 2: launch_packed_wave<QN, 2>(g, lay, rows, n, k, ids, sat, ra, s); return true;
+        case 4: launch_packed_wave<QN, 4>(g, lay, rows, n, k, ids, sat, ra, s); return true;
+        case 8: launch_packed_wave<QN, 8>(g, lay, rows, n, k, ids, sat, ra, s); return true;
+        case 16: launch_packed_wave<QN, 16>(g, lay, rows, n, k, ids, sat, ra, s); return true;
         default: return false;
     }
 }
@@ -1203,16 +1301,16 @@ bool packed_wave_w(int world, const int32_t* g, Layout lay, int64_t rows, int32_
 // One wave per row for world in {1, 2, 4, 8, 16} and qn = ceil(n/64) slot
 // registers per rank, with qn * world <= 64; false: use the block kernel.
 bool dispatch_packed_wave(int qn, int world, const int32_t* g, Layout lay, int64_t rows, int32_t n,
-                          int32_t k, int32_t* ids, int32_t* sat, hipStream_t s) {
+                          int32_t k, int32_t* ids, int32_t* sat, const RowsArgs& ra, hipStream_t s) {
     switch (qn) {
-        case 1: return packed_wave_w<1>(world, g, lay, rows, n, k, ids, sat, s);
-        case 2: return packed_wave_w<2>(world, g, lay, rows, n, k, ids, sat, s);
-        case 3: return packed_wave_w<3>(world, g, lay, rows, n, k, ids, sat, s);
-        case 4: return packed_wave_w<4>(world, g, lay, rows, n, k, ids, sat, s);
-        case 5: return packed_wave_w<5>(world, g, lay, rows, n, k, ids, sat, s);
-        case 6: return packed_wave_w<6>(world, g, lay, rows, n, k, ids, sat, s);
-        case 7: return packed_wave_w<7>(world, g, lay, rows, n, k, ids, sat, s);
-        case 8: return packed_wave_w<8>(world, g, lay, rows, n, k, ids, sat, s);
+        case 1: return packed_wave_w<1>(world, g, lay, rows, n, k, ids, sat, ra, s);
+        case 2: return packed_wave_w<2>(world, g, lay, rows, n, k, ids, sat, ra, s);
+        case 3: return packed_wave_w<3>(world, g, lay, rows, n, k, ids, sat, ra, s);
+        case 4: return packed_wave_w<4>(world, g, lay, rows, n, k, ids, sat, ra, s);
+        case 5: return packed_wave_w<5>(world, g, lay, rows, n, k, ids, sat, ra, s);
+        case 6: return packed_wave_w<6>(world, g, lay, rows, n, k, ids, sat, ra, s);
+        case 7: return packed_wave_w<7>(world, g, lay, rows, n, k, ids, sat, ra, s);
+        case 8: return packed_wave_w<8>(world, g, lay, rows, n, k, ids, sat, ra, s);
         default: return false;
     }
 }
@@ -1242,15 +1340,17 @@ int launch_pack_pairs(const float* x, int64_t rows, int64_t cols, int64_t ld, co
 }
 
 int launch_merge_packed(const int32_t* gathered, bool row_major, int32_t world, int64_t rows,
-                        int32_t n, int32_t k, int32_t* out_ids, int32_t* sat_word, hipStream_t s) {
+                        int32_t n, int32_t k, int32_t* out_ids, int32_t* sat_word,
+                        const RowsArgs* rows_args, hipStream_t s) {
     if (rows == 0) return RTS_OK;
     const Layout lay = row_major ? Layout{1, world} : Layout{rows, 1};
+    const RowsArgs ra = rows_args ? *rows_args : RowsArgs{};
     if (dispatch_packed_wave((n + kWave - 1) / kWave, world, gathered, lay, rows, n, k, out_ids,
-                             sat_word, s))
+                             sat_word, ra, s))
         return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
     const int kpt = pick_kpt((int64_t)world * n);
     const int rc = dispatch_kpt<PackedLaunch>(kpt, gathered, lay, world, rows, n, k, out_ids,
-                                              sat_word, s);
+                                              sat_word, ra, s);
     if (rc != RTS_OK) return rc;
     return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
 }
@@ -1271,11 +1371,12 @@ int launch_rescue_push(const int32_t* local_packed, int32_t rank, int32_t world,
 
 int launch_merge_rescue(const int32_t* gathered, const int32_t* recv, int32_t world, int64_t rows,
                         int32_t n, int32_t k, const int32_t* sat_word, int32_t* out_ids,
-                        hipStream_t s) {
+                        const RowsArgs* rows_args, hipStream_t s) {
     if (rows == 0 || (k - 1) / n == 0) return RTS_OK;
     const int kpt = pick_kpt(rescue_candidates(world, n, k));
+    const RowsArgs ra = rows_args ? *rows_args : RowsArgs{};
     const int rc = dispatch_kpt<RescueLaunch>(kpt, gathered, recv, world, rows, n, k, sat_word,
-                                              out_ids, s);
+                                              out_ids, ra, s);
     if (rc != RTS_OK) return rc;
     return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
 }

@@ -472,3 +472,97 @@ def test_emit_rows_merge_workload(rts):
             assert np.array_equal(host(valid)[sample], e_valid)
         inside = (((ids // W) // B) < tab.shape[1]).sum(dim=1)
         assert torch.equal(total, inside.long()), "ranks do not partition the selected ids"
+
+
+# ---------------------------------------------------------------------------
+# Owned rows straight from the packed selects (fused emit_rows)
+# ---------------------------------------------------------------------------
+
+def _table(rng, nreq=7, cols=40):
+    t = rng.integers(0, 1 << 20, size=(nreq, cols)).astype(np.int32)
+    t[0, 0] = 0x7FFFFFF0
+    return t
+
+
+@pytest.mark.parametrize("world,n,k,B", [(8, 384, 2048, 64), (3, 96, 500, 16), (16, 64, 1024, 32),
+                                         (4, 2048, 1024, 128), (8, 64, 96, 8)])
+def test_merge_select_rows_fused(rts, world, n, k, B):
+    rng = np.random.default_rng(world * 5 + n + k)
+    rows = 37
+    g = _gathered(rng, world, rows, n, 0.9, ties=bool(world % 2))
+    table = _table(rng)
+    req = rng.integers(-1, table.shape[0] + 1, size=rows).astype(np.int32)
+    eids, esat = oracle.merge_select_rank_major(g, k)
+    g_d, req_d, tab_d = dev(g), dev(req), dev(table)
+    stride = int(rng.integers(1, 500))
+    for rank in sorted({0, world - 1}):
+        say("fused rows", world, n, k, B, rank)
+        ids = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+        sat = torch.empty((rows,), dtype=torch.int32, device="cuda")
+        rows_out = torch.full((rows, k + 3), 777, dtype=torch.int32, device="cuda")
+        _, valid, _, _ = rts.merge_select_rank_major_rows(g_d, k, rank, req_d, tab_d, B, stride,
+                                                          rows_out=rows_out, out_ids=ids, sat_word=sat)
+        e_rows, e_valid = oracle.emit_rows(eids, world, rank, req, table, B, stride, k + 3)
+        assert_ids_equal(host(rows_out), e_rows, "rows_out")
+        assert np.array_equal(host(valid), e_valid), "valid_out"
+        assert_ids_equal(host(ids), eids, "ids")
+        assert np.array_equal(host(sat), esat), "sat_word"
+        # rows only: ids and sat_word not requested
+        r2, v2, _, _ = rts.merge_select_rank_major_rows(g_d, k, rank, req_d, tab_d, B, stride)
+        assert_ids_equal(host(r2), e_rows[:, :k], "rows_out without ids")
+        assert np.array_equal(host(v2), e_valid)
+
+
+def test_merge_rescue_rows_fused(rts):
+    world, n, k, B = 8, 384, 2048, 64
+    rng = np.random.default_rng(21)
+    rows, slots = 40, (k - 1) // n
+    g = _gathered(rng, world, rows, n, 1.0)
+    recv = np.ascontiguousarray(_gathered(rng, slots, rows, k, 0.95).transpose(1, 0, 2))
+    sw = _sat_words(rng, rows, world, n, k, g)
+    table = _table(rng, cols=300)
+    req = rng.integers(0, table.shape[0], size=rows).astype(np.int32)
+    ids0 = rng.integers(-1, 1 << 20, size=(rows, k)).astype(np.int32)
+    e_ids = oracle.merge_rescue_rank_major(g, recv, sw, ids0)
+    entered = e_ids.tolist() != ids0.tolist()
+    swu = sw.view(np.uint32)
+    mask = swu >> 16
+    enter = (mask != 0) & ((mask >> world) == 0) & (np.array([bin(int(m)).count("1") for m in mask]) <= slots)
+    for rank in (0, 5):
+        say("fused rescue rows", rank)
+        rows_out = torch.full((rows, k), 55, dtype=torch.int32, device="cuda")
+        valid = torch.full((rows,), 66, dtype=torch.int32, device="cuda")
+        ids = dev(ids0)
+        rts.merge_rescue_rank_major_rows(dev(g), dev(recv), dev(sw), k, rank, dev(req), dev(table), B, B,
+                                         rows_out, valid, out_ids=ids)
+        e_rows, e_valid = oracle.emit_rows(e_ids, world, rank, req, table, B, B)
+        got_rows, got_valid = host(rows_out), host(valid)
+        assert_ids_equal(got_rows[enter], e_rows[enter], "rescued rows_out")
+        assert np.array_equal(got_valid[enter], e_valid[enter])
+        assert (got_rows[~enter] == 55).all() and (got_valid[~enter] == 66).all(), "rows that stay were written"
+        assert_ids_equal(host(ids), e_ids, "rescued ids")
+    assert entered
+
+
+def test_merge_rows_workload_all_ranks(rts):
+    # Merge workload: the fused select's rows equal emit_rows of the select's
+    # ids for every rank, over all 6710 rows.
+    W, R, N, K = datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_N, datagen.MERGE_K
+    rng = np.random.default_rng(5)
+    table = np.stack([rng.permutation(200000)[:256] for _ in range(97)]).astype(np.int32)
+    req = (np.arange(R) % 97).astype(np.int32)
+    say("fused rows workload: generate")
+    ranks16 = datagen.bf16_bits(datagen.rank_slices(datagen.merge_global(), W))
+    x16 = bf16_dev(ranks16)
+    del ranks16
+    gathered = torch.empty((W, R, N + N // 32), dtype=torch.int32, device="cuda")
+    for r in range(W):
+        rts.pack_candidates(x16[r], rts.topk_rows(x16[r], N), out=gathered[r])
+    del x16
+    ids, _ = rts.merge_select_rank_major(gathered, K)
+    req_d, tab_d = dev(req), dev(table)
+    for rank in range(W):
+        say("fused rows workload rank", rank)
+        two_rows, two_valid = rts.emit_rows(ids, W, rank, req_d, tab_d, 64, 64)
+        f_rows, f_valid, _, _ = rts.merge_select_rank_major_rows(gathered, K, rank, req_d, tab_d, 64, 64)
+        assert torch.equal(f_rows, two_rows) and torch.equal(f_valid, two_valid), rank
