@@ -16,7 +16,12 @@ LIB = os.path.join(ROOT, "row_top_select_amd", "librow_top_select.so")
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from row_top_select_amd import build as b
+        # by path: importing the package would first load the missing library
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_rts_build", os.path.join(ROOT, "row_top_select_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build(verbose=False)
     lib = ctypes.CDLL(LIB)
     i64, i32, p, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
@@ -25,6 +30,13 @@ def lib():
     lib.merge_select_rank_major.argtypes = [p, i32, i64, i32, i32, p, p, p]
     lib.pack_pairs.argtypes = [p, i64, i64, i64, p, i32, i64, p, i32, i32, p, p]
     lib.merge_select_pairs_rank_major.argtypes = [p, i32, i64, i32, i32, p, p]
+    lib.merge_select_row_major.argtypes = [p, i32, i64, i32, i32, p, p, p]
+    lib.merge_select_pairs_row_major.argtypes = [p, i32, i64, i32, i32, p, p]
+    lib.rescue_push.argtypes = [p, i32, i32, i64, i32, i32, p, p, p]
+    lib.merge_rescue_rank_major.argtypes = [p, p, i32, i64, i32, i32, p, p, p]
+    lib.emit_rows.argtypes = [p, i64, i32, i32, i32, p, p, i64, i32, i64, i32, i64, p, i32, p, p]
+    lib.merge_select_rank_major_rows.argtypes = [p, i32, i64, i32, i32, p, p, p, p]
+    lib.merge_rescue_rank_major_rows.argtypes = [p, p, i32, i64, i32, i32, p, p, p, p]
     lib.topk_rows_workspace_size.argtypes = [ctypes.c_int, i64, i64, i32]
     lib.topk_rows_workspace_size.restype = sz
     lib.rts_status_string.argtypes = [ctypes.c_int]
@@ -44,7 +56,10 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"topk_rows", "pack_candidates", "merge_select_rank_major", "pack_pairs",
                           "merge_select_pairs_rank_major", "topk_rows_workspace_size",
-                          "rts_status_string"}
+                          "rts_status_string", "merge_select_row_major",
+                          "merge_select_pairs_row_major", "rescue_push", "merge_rescue_rank_major",
+                          "emit_rows", "merge_select_rank_major_rows",
+                          "merge_rescue_rank_major_rows"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -101,3 +116,46 @@ def test_merge_and_pack_validation(lib):
                           None) == EUNSUP                                                  # gid range
     assert lib.merge_select_pairs_rank_major(FAKE, 8, 4, 8192, 512, FAKE, None) == EUNSUP
     assert lib.merge_select_pairs_rank_major(FAKE, 8, 4, 64, 0, FAKE, None) == EINVAL
+
+
+class KvRows(ctypes.Structure):
+    """rts_kv_rows, restated from the header."""
+    _fields_ = [("dcp_rank", ctypes.c_int32), ("req_id", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("table_rows", ctypes.c_int64),
+                ("table_cols", ctypes.c_int32), ("ld_table", ctypes.c_int64),
+                ("block_size", ctypes.c_int32), ("stride_rows", ctypes.c_int64),
+                ("rows_out", ctypes.c_void_p), ("out_cols", ctypes.c_int32),
+                ("valid_out", ctypes.c_void_p)]
+
+
+def test_second_round_layout_and_rows_validation(lib):
+    EINVAL, EUNSUP = -1, -2
+    # row-major selects share the rank-major checks
+    assert lib.merge_select_row_major(FAKE, 17, 4, 32, 64, FAKE, None, None) == EINVAL
+    assert lib.merge_select_pairs_row_major(FAKE, 8, 4, 8192, 512, FAKE, None) == EUNSUP
+    # push: rank outside the world, k not a multiple of 32, null recv
+    assert lib.rescue_push(FAKE, 8, 8, 4, 384, 2048, FAKE, FAKE, None) == EINVAL
+    assert lib.rescue_push(FAKE, 0, 8, 4, 384, 2000, FAKE, FAKE, None) == EINVAL
+    assert lib.rescue_push(FAKE, 0, 8, 4, 384, 2048, FAKE, None, None) == EINVAL
+    assert lib.rescue_push(FAKE, 0, 8, 4, 4096, 2048, FAKE, FAKE, None) == 0    # no slots: no-op
+    # rescue: too many candidate slots, null sat_word
+    assert lib.merge_rescue_rank_major(FAKE, FAKE, 16, 4, 32, 2048, FAKE, FAKE, None) == EUNSUP
+    assert lib.merge_rescue_rank_major(FAKE, FAKE, 8, 4, 384, 2048, None, FAKE, None) == EINVAL
+    # emit_rows: rank >= world, out_cols < k, block_size 0, ld_table < cols
+    assert lib.emit_rows(FAKE, 4, 64, 8, 8, FAKE, FAKE, 2, 4, 4, 64, 64, FAKE, 64, FAKE, None) == EINVAL
+    assert lib.emit_rows(FAKE, 4, 64, 8, 0, FAKE, FAKE, 2, 4, 4, 64, 64, FAKE, 63, FAKE, None) == EINVAL
+    assert lib.emit_rows(FAKE, 4, 64, 8, 0, FAKE, FAKE, 2, 4, 4, 0, 64, FAKE, 64, FAKE, None) == EINVAL
+    assert lib.emit_rows(FAKE, 4, 64, 8, 0, FAKE, FAKE, 2, 4, 3, 64, 64, FAKE, 64, FAKE, None) == EINVAL
+    assert lib.emit_rows(FAKE, 4, 4096, 8, 0, FAKE, FAKE, 2, 4, 4, 64, 64, FAKE, 4096, FAKE,
+                         None) == EUNSUP
+    # fused rows: a missing or invalid rts_kv_rows
+    assert lib.merge_select_rank_major_rows(FAKE, 8, 4, 384, 2048, None, None, None, None) == EINVAL
+    kv = KvRows(8, FAKE.value, FAKE.value, 2, 4, 4, 64, 64, FAKE.value, 2048, FAKE.value)   # rank 8
+    assert lib.merge_select_rank_major_rows(FAKE, 8, 4, 384, 2048, ctypes.byref(kv), None, None,
+                                            None) == EINVAL
+    kv.dcp_rank, kv.out_cols = 3, 2047                                                   # out_cols < k
+    assert lib.merge_select_rank_major_rows(FAKE, 8, 4, 384, 2048, ctypes.byref(kv), None, None,
+                                            None) == EINVAL
+    kv.out_cols, kv.rows_out = 2048, None                                                # null rows_out
+    assert lib.merge_rescue_rank_major_rows(FAKE, FAKE, 8, 4, 384, 2048, FAKE, ctypes.byref(kv),
+                                            None, None) == EINVAL
