@@ -6,12 +6,16 @@ Headline workload: top-512 of every row of a 4096 x 102400 fp32 logit matrix
 whole matrix, inputs resident in HBM.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--all] [--copy-calib]
+                  [--counters NAME]
 
---all adds the other workloads (prefill, ties, long, decode, the 8K x 8K
-distribution ablation, the headline shape in bf16, packed and pair merges, the
-merge's second round) as a
-"secondary" object; --copy-calib only runs a plain 1 GiB device
-copy (the reference point for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling).
+--all adds a "secondary" object with the other workloads: tiny, prefill,
+ties, long, decode, the 8K x 8K distribution ablation, the headline shape in
+bf16, the packed and pair merges with their row-major comparison, the merge's
+second round and the owned-rows output (warm back-to-back timings, plus
+cold-cache medians for the selects).  --copy-calib only runs a plain 1 GiB
+device copy (the reference point for rocprofv3 FETCH_SIZE / WRITE_SIZE
+scaling).  --counters NAME only runs one workload's measured call three times,
+for rocprofv3 --pmc runs.
 """
 
 from __future__ import annotations
@@ -63,6 +67,42 @@ def time_calls(fn, steps, warmup, torch):
     return wall, ev0.elapsed_time(ev1) / 1e3 / steps
 
 
+_SCRUB = None
+
+
+def time_cold(fn, calls, torch):
+    """Median per-call time with the caches cold: a 1 GiB read-modify-write
+    (larger than L2 and the 256 MB Infinity Cache) runs before each timed call,
+    which alone sits between two events on the launch stream."""
+    global _SCRUB
+    if _SCRUB is None:
+        _SCRUB = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn()
+    ts = []
+    for _ in range(calls):
+        _SCRUB.add_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def time_graph(fn, steps, torch):
     """Per-call time of ``fn`` replayed from a HIP graph of ``steps`` calls: for
     kernels of a few microseconds, where launching from Python one call at a
@@ -102,7 +142,8 @@ def cpu_baseline(x_sample, ends_sample, k, total_rows_note):
         "unit": "rows/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": f"{what} of the same workload (same data and row ends), one run, {dt:.2f} s wall",
+        "sample": f"{what} of the same workload (same data and row ends), one run, {dt:.2f} s wall; "
+                  f"host CPU {cpu_model()}",
     }
 
 
@@ -111,7 +152,7 @@ def secondary(torch, rts, datagen, steps, warmup):
     res = {}
     # The measured configs, the pages' distribution ablation (8K x 8K: normal,
     # +100, *1e-8) and the headline shape in bf16.
-    for name in ("prefill", "ties", "long", "decode", "robust", "robust_plus100",
+    for name in ("tiny", "prefill", "ties", "long", "decode", "robust", "robust_plus100",
                  "robust_scale1e8", "verylong_bf16"):
         bf16 = name.endswith("_bf16")
         w = datagen.WORKLOADS[name[:-5] if bf16 else name]
@@ -126,13 +167,14 @@ def secondary(torch, rts, datagen, steps, warmup):
         out = torch.empty((w.rows, w.k), dtype=torch.int32, device="cuda")
         ws_n = rts.topk_rows_workspace_size(x.dtype, w.rows, w.cols, w.k)
         ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
-        _, t = time_calls(lambda: rts.topk_rows(x, w.k, row_ends=ends, out=out,
-                                                workspace=ws if ws_n else None),
-                          steps, warmup, torch)
+        call = lambda: rts.topk_rows(x, w.k, row_ends=ends, out=out, workspace=ws if ws_n else None)
+        _, t = time_calls(call, steps, warmup, torch)
+        t_cold = time_cold(call, 9, torch)
         b = algorithmic_bytes(ends_np, w.k, w.rows, elem=2 if bf16 else 4)
         res[name] = {"shape": [w.rows, w.cols], "k": w.k, "dtype": "bf16" if bf16 else "f32",
                      "us_per_call": t * 1e6, "rows_per_s": w.rows / t,
-                     "algorithmic_GBps": b / t / 1e9}
+                     "algorithmic_GBps": b / t / 1e9, "cold_us_per_call": t_cold * 1e6,
+                     "cold_algorithmic_GBps": b / t_cold / 1e9}
         del x
     # Packed merge (config of 8 simulated ranks) and the pair merge.
     W, R, S, N, K = (datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_LOCAL_COLS,
@@ -152,6 +194,8 @@ def secondary(torch, rts, datagen, steps, warmup):
     sat = torch.empty((R,), dtype=torch.int32, device="cuda")
     _, t_sel = time_calls(lambda: rts.merge_select_rank_major(gathered, K, out=ids, sat_word=sat),
                           steps, warmup, torch)
+    t_sel_cold = time_cold(lambda: rts.merge_select_rank_major(gathered, K, out=ids, sat_word=sat), 9,
+                           torch)
     sel_bytes = W * R * (N + N // 32) * 4 + R * K * 4 + R * 4
     # The same words reordered row-major [R, W, n + n/32] (the dim-1 gather's
     # layout): the reorder copy, and the select reading that layout.
@@ -187,6 +231,7 @@ def secondary(torch, rts, datagen, steps, warmup):
     res["merge_packed"] = {"shape": [W, R, N + N // 32], "k": K,
                            "select_us": t_sel * 1e6, "select_rows_per_s": R / t_sel,
                            "select_algorithmic_GBps": sel_bytes / t_sel / 1e9,
+                           "select_cold_us": t_sel_cold * 1e6,
                            "row_major_select_us": t_sel_rm * 1e6,
                            "reorder_copy_us": t_copy * 1e6,
                            "reorder_copy_plus_row_major_select_us": (t_copy + t_sel_rm) * 1e6,
@@ -230,6 +275,7 @@ def secondary(torch, rts, datagen, steps, warmup):
     pid = torch.empty((R, K), dtype=torch.int32, device="cuda")
     _, t_pairs = time_calls(lambda: rts.merge_select_pairs_rank_major(pairs, K, out=pid), steps,
                             warmup, torch)
+    t_pairs_cold = time_cold(lambda: rts.merge_select_pairs_rank_major(pairs, K, out=pid), 9, torch)
     pb = W * R * K * 8 + R * K * 4
     del x32
     prm = torch.empty((R, W * K, 2), dtype=torch.int32, device="cuda")
@@ -241,11 +287,59 @@ def secondary(torch, rts, datagen, steps, warmup):
     res["merge_pairs"] = {"shape": [W, R, K, 2], "k": K, "select_us": t_pairs * 1e6,
                           "select_rows_per_s": R / t_pairs,
                           "select_algorithmic_GBps": pb / t_pairs / 1e9,
+                          "select_cold_us": t_pairs_cold * 1e6,
                           "row_major_select_us": t_pairs_rm * 1e6,
                           "reorder_copy_us": t_pcopy * 1e6,
                           "reorder_copy_plus_row_major_select_us": (t_pcopy + t_pairs_rm) * 1e6,
                           "row_major_ids_identical": bool(torch.equal(pid_rm, pid))}
     return res
+
+
+COUNTER_WORKLOADS = ("tiny", "prefill", "ties", "long", "decode", "robust", "robust_plus100",
+                     "robust_scale1e8", "verylong", "verylong_bf16", "merge_packed", "merge_pairs")
+
+
+def counters_run(name, torch, rts, datagen, calls=3):
+    """Only the measured call of one workload, `calls` times (for rocprofv3 --pmc runs)."""
+    import numpy as np
+    if name in ("merge_packed", "merge_pairs"):
+        W, R, N, K = datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_N, datagen.MERGE_K
+        g = datagen.merge_global()
+        ranks32 = datagen.rank_slices(g, W)
+        del g
+        if name == "merge_packed":
+            x = torch.from_numpy(datagen.bf16_bits(ranks32).view(np.int16)).cuda().view(torch.bfloat16)
+            buf = torch.empty((W, R, N + N // 32), dtype=torch.int32, device="cuda")
+            for r in range(W):
+                rts.pack_candidates(x[r], rts.topk_rows(x[r], N), out=buf[r])
+            op = lambda: rts.merge_select_rank_major(buf, K, out=ids, sat_word=sat)
+            sat = torch.empty((R,), dtype=torch.int32, device="cuda")
+        else:
+            x = torch.from_numpy(ranks32).cuda()
+            buf = torch.empty((W, R, K, 2), dtype=torch.int32, device="cuda")
+            for r in range(W):
+                rts.pack_pairs(x[r], rts.topk_rows(x[r], K), r, W, out=buf[r])
+            op = lambda: rts.merge_select_pairs_rank_major(buf, K, out=ids)
+        ids = torch.empty((R, K), dtype=torch.int32, device="cuda")
+        del x
+    else:
+        bf16 = name.endswith("_bf16")
+        w = datagen.WORKLOADS[name[:-5] if bf16 else name]
+        x_np = datagen.logits(w, threads=8)
+        if bf16:
+            x = torch.from_numpy(datagen.bf16_bits(x_np).view(np.int16)).cuda().view(torch.bfloat16)
+        else:
+            x = torch.from_numpy(x_np).cuda()
+        ends = torch.from_numpy(datagen.row_ends(w)).cuda()
+        out = torch.empty((w.rows, w.k), dtype=torch.int32, device="cuda")
+        ws_n = rts.topk_rows_workspace_size(x.dtype, w.rows, w.cols, w.k)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+        op = lambda: rts.topk_rows(x, w.k, row_ends=ends, out=out, workspace=ws if ws_n else None)
+    torch.cuda.synchronize()
+    for _ in range(calls):
+        op()
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_workload": name, "calls": calls}))
 
 
 def main():
@@ -256,6 +350,8 @@ def main():
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--counters", choices=COUNTER_WORKLOADS,
+                    help="only run one workload's measured call 3 times (for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
@@ -279,6 +375,10 @@ def main():
 
     import datagen
     import row_top_select_amd as rts
+
+    if args.counters:
+        counters_run(args.counters, torch, rts, datagen)
+        return
 
     w = datagen.WORKLOADS["verylong"]
     x_np = datagen.logits(w, threads=8)
