@@ -147,6 +147,27 @@ def cpu_baseline(x_sample, ends_sample, k, total_rows_note):
     }
 
 
+def oracle_times(datagen):
+    """The oracle on tiny and prefill, on one thread and on all of them:
+    median of 3 timed runs after 1 warm-up (test infrastructure, CPU only)."""
+    import oracle
+    res = {"cores": oracle.max_threads(), "cpu": cpu_model()}
+    for name in ("tiny", "prefill"):
+        w = datagen.WORKLOADS[name]
+        x = datagen.logits(w, threads=8)
+        ends = datagen.row_ends(w)
+        for threads in (1, oracle.max_threads()):
+            ts = []
+            for i in range(4):
+                t0 = time.perf_counter()
+                oracle.topk_rows(x, ends, w.k, nthreads=threads)
+                if i:
+                    ts.append(time.perf_counter() - t0)
+            ts.sort()
+            res[f"{name}_{threads}_threads_ms"] = ts[1] * 1e3
+    return res
+
+
 def secondary(torch, rts, datagen, steps, warmup):
     import numpy as np
     res = {}
@@ -436,6 +457,8 @@ def main():
         del x
         torch.cuda.empty_cache()
         result["secondary"] = secondary(torch, rts, datagen, max(5, args.steps // 5), 2)
+        if not args.no_cpu:
+            result["secondary"]["cpu_oracle"] = oracle_times(datagen)
     print(json.dumps(result))
 
 
