@@ -621,20 +621,20 @@ TopkPlan plan_topk_rows(int dtype, int64_t rows, int64_t cols, int32_t k, bool a
     (void)dtype;
     TopkPlan p{list_e(k), 1, 1, 0};
     const int64_t lp = (int64_t)kWave * p.e;
-    // Keep pieces long enough that compactions stay a small part of the work.
-    const int64_t min_piece = lp * 8 > 4096 ? lp * 8 : 4096;
-    int64_t max_pieces = cols / min_piece;
-    if (max_pieces < 1) max_pieces = 1;
     const int64_t want = rows > 0 ? (kTargetWaves + rows - 1) / rows : 1;
-    const int64_t pieces = want < max_pieces ? want : max_pieces;
-    if (pieces >= 4) {
-        p.waves = 4;
-        int64_t gr = (pieces + 3) / 4;
-        if (!allow_split || gr < 2) gr = 1;
+    // Pieces long enough that compactions stay a small part of the work: the
+    // waves of one workgroup share their threshold through LDS, so their
+    // pieces may be shorter than those of separate workgroups, whose lists
+    // also go through the workspace and a merge kernel.
+    const int64_t wg_piece = lp * 4 > 2048 ? lp * 4 : 2048;
+    const int64_t grp_piece = lp * 8 > 6400 ? lp * 8 : 6400;
+    const int64_t per_wg = want < cols / wg_piece ? want : cols / wg_piece;
+    p.waves = per_wg >= 4 ? 4 : per_wg >= 2 ? 2 : 1;
+    if (p.waves == 4 && allow_split) {
+        const int64_t by_len = cols / (4 * grp_piece);
+        int64_t gr = want / 4 < by_len ? want / 4 : by_len;
         if (gr > 256) gr = 256;
-        p.groups = (int)gr;
-    } else if (pieces >= 2) {
-        p.waves = 2;
+        if (gr >= 2) p.groups = (int)gr;
     }
     if (p.groups > 1) p.ws_bytes = (size_t)rows * p.groups * lp * sizeof(uint64_t);
     return p;
