@@ -894,19 +894,28 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
 
 // ---------------------------------------------------------------------------
 // Pair select: one wave per rank, the `world` waves of a workgroup share a
-// row.  Lane l of wave r holds candidate j = q*64 + l of rank r as a 32-bit
-// score key (0 = empty) and its gid in key[q], gid[q]; wave order, register
-// order, lane order is candidate order.
-//   1. Score threshold: 256-bin levels over the keys in [min, max] of the
-//      valid ones; atomics into 8 lane-striped copies, wave 0 sums them and
-//      finds the bin, three barriers per level.
-//   2. Ties at the k-th key: up to 64 tied candidates are sorted by gid in
-//      wave 0; more go through levels over 2^31-1-gid.
-//   3. Emission: per-wave selected counts, an exclusive scan over the waves,
-//      then running count + mbcnt positions; -1 tail.
+// row.  Lane l of wave r holds
+// candidate j = q*64 + l of rank r as a 32-bit score key (0 = empty) and its
+// gid in key[q], gid[q]; wave order, register order, lane order is candidate
+// order.  Per row:
+//   1. One 256-bin level over the keys in [min, max] of the valid ones
+//      (atomics into 8 lane-striped copies) finds the bin B holding the k-th
+//      key.
+//   2. The candidates in bin B or above (the k - need above it plus B's own)
+//      are compacted in candidate order into an LDS list; the rest of the row
+//      runs on the list (about k entries instead of world * kc registers).
+//   3. Further levels over the list entries inside B; ties at the k-th key
+//      are sorted by gid in one wave (up to 64) or resolved by levels over
+//      the gid.
+//   4. Emission in candidate order: each wave emits its own list segment at
+//      an offset from the selected counts of the waves before it.
+// A row with at most k valid candidates, or whose list would not fit (heavy
+// ties), runs the same levels, tie rule and emission over the row re-read
+// from memory, so that no candidate registers are held across them.
 // ---------------------------------------------------------------------------
 constexpr int kPairCopies = 8;
 constexpr int kPairStride = 257;
+constexpr int kPairListCap = 4096;
 
 struct PairSmem {
     uint32_t hist[kPairCopies][kPairStride];
@@ -915,29 +924,38 @@ struct PairSmem {
     uint32_t bc[4];
     uint32_t tied[kWave];
     uint32_t ntied;
+    uint32_t woff[16];  // per-wave list entries
+    uint32_t wsel[16];  // per-wave selected entries
+    uint32_t lkey[kPairListCap];
+    uint32_t lgid[kPairListCap];
 };
 
-// Counts key - wlo (in [0, span]) into bin (key - wlo) >> sh for the entries
-// where `take` holds, then wave 0 finds the bin reaching `need` from the top.
-// Returns (uniform) ok, bin, cb; lowers need.
-template <int QK, typename KeyF>
-__device__ __forceinline__ bool block_radix_level(PairSmem& sm, KeyF keyf, uint32_t wlo,
-                                                  uint32_t span, uint32_t sh, int& need,
-                                                  uint32_t& bin, uint32_t& cb) {
+// The k selected candidates: key > thr_gt, or key == tie_key and gid <= gid_cut.
+struct PairCut {
+    uint32_t thr_gt, tie_key, gid_cut;
+};
+
+__device__ __forceinline__ bool pair_selected(uint32_t key, uint32_t gid, const PairCut& c) {
+    return key != 0u && (key > c.thr_gt || (key == c.tie_key && gid <= c.gid_cut));
+}
+
+// Counts key - wlo, when it lies in [0, span], into bin (key - wlo) >> sh.
+__device__ __forceinline__ void pair_hist_add(PairSmem& sm, uint32_t key, uint32_t wlo,
+                                              uint32_t span, uint32_t sh) {
+    const uint32_t x = key - wlo;
+    if (x <= span)
+        __hip_atomic_fetch_add(&sm.hist[lane_id() & (kPairCopies - 1)][x >> sh], 1u,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// All threads, after their pair_hist_add calls: sums (and clears) the copies,
+// then wave 0 finds the bin where the count from the top reaches need.
+// Returns (uniform) ok, the bin and its count, and lowers need by the count
+// above the bin.
+__device__ __forceinline__ bool pair_hist_find(PairSmem& sm, int& need, uint32_t& bin, uint32_t& cb) {
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
-    uint32_t* hc = sm.hist[lane & (kPairCopies - 1)];
-#pragma unroll
-    for (int q = 0; q < QK; ++q) {
-        uint32_t key;
-        if (keyf(q, key)) {
-            const uint32_t x = key - wlo;
-            if (x <= span)
-                __hip_atomic_fetch_add(&hc[x >> sh], 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-    }
-    __syncthreads();
+    lds_barrier();
     for (int b = threadIdx.x; b < 256; b += blockDim.x) {  // the block may have < 256 threads
         uint32_t t = 0;
 #pragma unroll
@@ -947,7 +965,7 @@ __device__ __forceinline__ bool block_radix_level(PairSmem& sm, KeyF keyf, uint3
         }
         sm.bins[b] = t;
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
         int nd = need;
         uint32_t b, c;
@@ -959,44 +977,200 @@ __device__ __forceinline__ bool block_radix_level(PairSmem& sm, KeyF keyf, uint3
             sm.bc[3] = (uint32_t)nd;
         }
     }
-    __syncthreads();
+    lds_barrier();
     const bool ok = sm.bc[0] != 0u;
     bin = sm.bc[1];
     cb = sm.bc[2];
     if (ok) need = (int)sm.bc[3];
-    __syncthreads();  // sm.bc is rewritten by the next level
+    lds_barrier();  // sm.bc is rewritten by the next level
     return ok;
 }
 
+// Radix levels over the keys that `visit` hands out (visit(f) calls
+// f(key, gid) for each of this thread's entries), starting from the window
+// [wlo, wlo + span] in bins of 2^sh: ends with either a plain threshold (the
+// k selected are the keys > thr_gt) or ties at tie_key, ntie of them, of which
+// the `need` lowest gids are selected.
+template <typename Visit>
+__device__ __forceinline__ void pair_levels(PairSmem& sm, Visit visit, int& need, uint32_t wlo,
+                                            uint32_t span, uint32_t sh, uint32_t mx, uint32_t& thr_gt,
+                                            bool& ties, uint32_t& tie_key, uint32_t& ntie) {
+    ties = false;
+    tie_key = 0u;
+    ntie = 0u;
+    thr_gt = wlo - 1u;
+#pragma unroll 1
+    for (int level = 0; level < 4; ++level) {  // a 32-bit key needs four at most
+        visit([&](uint32_t key, uint32_t) __attribute__((always_inline)) { pair_hist_add(sm, key, wlo, span, sh); });
+        uint32_t bin, cb;
+        if (!pair_hist_find(sm, need, bin, cb)) {
+            thr_gt = wlo - 1u;
+            return;
+        }
+        const uint32_t blo = wlo + (bin << sh);
+        if ((int)cb == need) {
+            thr_gt = blo - 1u;
+            return;
+        }
+        if (sh == 0) {
+            thr_gt = blo;
+            tie_key = blo;
+            ties = true;
+            ntie = cb;
+            return;
+        }
+        wlo = blo;
+        const uint32_t top = mx - blo, width1 = (1u << sh) - 1u;
+        span = width1 < top ? width1 : top;
+        sh = sh > 8 ? sh - 8 : 0u;
+    }
+}
+
+// The largest gid taken among the ntie entries with key == tie_key, when the
+// `need` lowest gids are taken: a wave sort for up to 64, else levels over
+// 2^31 - 1 - gid.
+template <typename Visit>
+__device__ __forceinline__ uint32_t pair_tie_cut(PairSmem& sm, Visit visit, uint32_t tie_key,
+                                                 uint32_t ntie, int need) {
+    const int lane = lane_id();
+    if (ntie <= (uint32_t)kWave) {
+        visit([&](uint32_t key, uint32_t gid) __attribute__((always_inline)) {
+            if (key == tie_key) {
+                const uint32_t s = __hip_atomic_fetch_add(&sm.ntied, 1u, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (s < (uint32_t)kWave) sm.tied[s] = gid;
+            }
+        });
+        lds_barrier();
+        if (threadIdx.x < (unsigned)kWave) {
+            uint64_t sv[1] = {lane < (int)ntie ? (uint64_t)sm.tied[lane] : ~0ull};
+            wave_bitonic_sort<1, false>(sv);
+            const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sv[0], need - 1);
+            if (lane == 0) {
+                sm.bc[0] = c;
+                sm.ntied = 0u;
+            }
+        }
+        lds_barrier();
+        const uint32_t cut = sm.bc[0];
+        lds_barrier();
+        return cut;
+    }
+    uint32_t gw = 0u, gspan = 0x7FFFFFFFu, gs = 23u;
+#pragma unroll 1
+    for (int gl = 0; gl < 4; ++gl) {
+        visit([&](uint32_t key, uint32_t gid) __attribute__((always_inline)) {
+            if (key == tie_key) pair_hist_add(sm, 0x7FFFFFFFu - gid, gw, gspan, gs);
+        });
+        uint32_t gbin, gcb;
+        if (!pair_hist_find(sm, need, gbin, gcb)) break;
+        gw += gbin << gs;
+        if ((int)gcb == need || gs == 0) break;
+        gspan = (1u << gs) - 1u;
+        gs = gs > 8 ? gs - 8 : 0u;
+    }
+    return 0x7FFFFFFFu - gw;
+}
+
+// Emission in candidate order from a visitor that hands out this lane's
+// candidates register by register in a uniform loop (so ballots see the whole
+// wave); -1 after the selected ones.
+template <typename Visit>
+__device__ __forceinline__ void pair_emit_visit(PairSmem& sm, Visit visit, const PairCut& c, int world,
+                                                int k, int32_t* __restrict__ o_row) {
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    uint32_t cnt = 0;
+    visit([&](uint32_t key, uint32_t gid) __attribute__((always_inline)) {
+        cnt += (uint32_t)__popcll(__ballot(pair_selected(key, gid, c)));
+    });
+    if (lane == 0) sm.red[wave][3] = cnt;
+    lds_barrier();
+    uint32_t base = 0, total = 0;
+    for (int w = 0; w < world; ++w) {
+        const uint32_t n = sm.red[w][3];
+        base += w < wave ? n : 0u;
+        total += n;
+    }
+    visit([&](uint32_t key, uint32_t gid) __attribute__((always_inline)) {
+        const bool sel = pair_selected(key, gid, c);
+        const uint64_t m = __ballot(sel);
+        const uint32_t pos = base + mbcnt64(m);
+        if (sel && pos < (uint32_t)k) o_row[pos] = (int32_t)gid;
+        base += (uint32_t)__popcll(m);
+    });
+    for (int p = (int)(total < (uint32_t)k ? total : (uint32_t)k) + (int)threadIdx.x; p < k;
+         p += kWave * world)
+        o_row[p] = -1;
+}
+
+// Emission from the LDS list in candidate order: wave w's segment holds its
+// rank's listed candidates; -1 after the selected ones (not reached when the
+// counts are consistent).
+__device__ __forceinline__ void pair_emit_list(PairSmem& sm, const PairCut& c, int world, int k,
+                                               int32_t* __restrict__ o_row) {
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    uint32_t off = 0;
+    for (int w = 0; w < wave; ++w) off += sm.woff[w];
+    const uint32_t n = sm.woff[wave];
+    uint32_t cnt = 0;
+#pragma unroll 1
+    for (uint32_t b = 0; b < n; b += kWave) {
+        const bool in = b + (uint32_t)lane < n && off + b + (uint32_t)lane < (uint32_t)kPairListCap;
+        const uint32_t i = in ? off + b + (uint32_t)lane : 0u;
+        const bool sel = in && pair_selected(sm.lkey[i], sm.lgid[i], c);
+        cnt += (uint32_t)__popcll(__ballot(sel));
+    }
+    if (lane == 0) sm.wsel[wave] = cnt;
+    lds_barrier();
+    uint32_t base = 0, total = 0;
+    for (int w = 0; w < world; ++w) {
+        const uint32_t s = sm.wsel[w];
+        base += w < wave ? s : 0u;
+        total += s;
+    }
+#pragma unroll 1
+    for (uint32_t b = 0; b < n; b += kWave) {
+        const bool in = b + (uint32_t)lane < n && off + b + (uint32_t)lane < (uint32_t)kPairListCap;
+        const uint32_t i = in ? off + b + (uint32_t)lane : 0u;
+        const uint32_t gid = sm.lgid[i];
+        const bool sel = in && pair_selected(sm.lkey[i], gid, c);
+        const uint64_t m = __ballot(sel);
+        const uint32_t pos = base + mbcnt64(m);
+        if (sel && pos < (uint32_t)k) o_row[pos] = (int32_t)gid;
+        base += (uint32_t)__popcll(m);
+    }
+    for (int p = (int)(total < (uint32_t)k ? total : (uint32_t)k) + (int)threadIdx.x; p < k;
+         p += kWave * world)
+        o_row[p] = -1;
+}
+
 template <int QK>
-__global__ __launch_bounds__(1024) void merge_pairs_wave_kernel(
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void merge_pairs_wave_kernel(
     const int32_t* __restrict__ pairs, Layout lay, int32_t world, int64_t rows, int32_t kc,
     int32_t k, int32_t* __restrict__ out_ids) {
     __shared__ PairSmem sm;
     typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;  // the rank
-    const int64_t row = blockIdx.x;
     const int nthreads = kWave * world;
 
     for (int q = threadIdx.x; q < kPairCopies * kPairStride; q += nthreads) (&sm.hist[0][0])[q] = 0u;
     if (threadIdx.x == 0) sm.ntied = 0u;
 
-    uint32_t key[QK], gid[QK];
-    {
-        const i32x2* src = reinterpret_cast<const i32x2*>(pairs) + lay.at(wave, row) * kc;
+    const int64_t row = blockIdx.x;
+    const i32x2* src = reinterpret_cast<const i32x2*>(pairs) + lay.at(wave, row) * kc;
+    uint32_t key[QK];
 #pragma unroll
-        for (int q = 0; q < QK; ++q) {
-            const int j = q * kWave + lane;
-            const bool in = j < kc;  // QK may exceed ceil(kc / 64)
-            const i32x2 pr = src[in ? j : 0];
-            const uint32_t u = (uint32_t)pr[0];
-            const bool valid = in && pr[1] >= 0 && !f32_bits_is_nan(u);
-            key[q] = valid ? key32_of_bits(u) : 0u;
-            gid[q] = (uint32_t)pr[1];
-        }
+    for (int q = 0; q < QK; ++q) {
+        const int j = q * kWave + lane;
+        const i32x2 pr = src[j < kc ? j : 0];  // QK may exceed ceil(kc / 64)
+        const uint32_t u = (uint32_t)pr[0];
+        const bool valid = j < kc && pr[1] >= 0 && !f32_bits_is_nan(u);
+        key[q] = valid ? key32_of_bits(u) : 0u;
     }
-    auto fresh = [&]() {
+    auto fresh = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < QK; ++q) asm volatile("" : "+v"(key[q]));
     };
@@ -1017,7 +1191,7 @@ __global__ __launch_bounds__(1024) void merge_pairs_wave_kernel(
         sm.red[wave][1] = mn;
         sm.red[wave][2] = mx;
     }
-    __syncthreads();
+    lds_barrier();
     nv = 0;
     mn = 0xFFFFFFFFu;
     mx = 0u;
@@ -1026,131 +1200,98 @@ __global__ __launch_bounds__(1024) void merge_pairs_wave_kernel(
         mn = sm.red[w][1] < mn ? sm.red[w][1] : mn;
         mx = sm.red[w][2] > mx ? sm.red[w][2] : mx;
     }
-    __syncthreads();
-
-    // Selection rule: key > thr_gt, or key == tie_key and gid <= gid_cut.
-    uint32_t thr_gt = 0u, tie_key = 0u, gid_cut = 0u;
-    if (nv > (uint32_t)k) {
-        int need = k;
-        bool open = true, ties = false;
-        uint32_t wlo = mn, span = mx - mn, ntie = 0u;
-        const int bl = span ? 32 - __clz((int)span) : 0;
-        uint32_t sh = bl > 8 ? (uint32_t)(bl - 8) : 0u;
-#pragma unroll
-        for (int level = 0; level < 4; ++level) {  // a 32-bit key needs four at most
-            fresh();
-            if (open) {
-                uint32_t bin, cb;
-                auto kf = [&](int q, uint32_t& v) { v = key[q]; return true; };
-                if (!block_radix_level<QK>(sm, kf, wlo, span, sh, need, bin, cb)) {
-                    thr_gt = wlo - 1u;
-                    open = false;
-                } else {
-                    const uint32_t blo = wlo + (bin << sh);
-                    if ((int)cb == need) {
-                        thr_gt = blo - 1u;
-                        open = false;
-                    } else if (sh == 0) {
-                        thr_gt = blo;
-                        tie_key = blo;
-                        ties = true;
-                        ntie = cb;
-                        open = false;
-                    } else {
-                        wlo = blo;
-                        const uint32_t top = mx - blo, width1 = (1u << sh) - 1u;
-                        span = width1 < top ? width1 : top;
-                        sh = sh > 8 ? sh - 8 : 0u;
-                    }
-                }
-            }
-        }
-        if (open) thr_gt = wlo - 1u;  // not reached
-        // Ties: up to 64 sorted by gid in wave 0, more through gid levels.
-        fresh();
-        if (ties && ntie <= (uint32_t)kWave) {
-#pragma unroll
-            for (int q = 0; q < QK; ++q) {
-                const bool t = key[q] == tie_key;
-                const uint64_t m = __ballot(t);
-                if (m) {
-                    uint32_t b0 = 0;
-                    if (lane == 0)
-                        b0 = __hip_atomic_fetch_add(&sm.ntied, (uint32_t)__popcll(m), __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_WORKGROUP);
-                    b0 = __builtin_amdgcn_readfirstlane(b0);
-                    const uint32_t slot = b0 + mbcnt64(m);
-                    if (t && slot < (uint32_t)kWave) sm.tied[slot] = gid[q];
-                }
-            }
-            __syncthreads();
-            if (wave == 0) {
-                uint64_t sv[1] = {lane < (int)ntie ? (uint64_t)sm.tied[lane] : ~0ull};
-                wave_bitonic_sort<1, false>(sv);
-                const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sv[0], need - 1);
-                if (lane == 0) sm.bc[0] = c;
-            }
-            __syncthreads();
-            gid_cut = sm.bc[0];
-            __syncthreads();
-        }
-        {
-            bool gopen = ties && ntie > (uint32_t)kWave;
-            uint32_t gw = 0u, gspan = 0x7FFFFFFFu, gs = 23u;
-#pragma unroll
-            for (int gl = 0; gl < 4; ++gl) {
-                fresh();
-                if (gopen) {
-                    uint32_t gbin, gcb;
-                    auto kf = [&](int q, uint32_t& v) {
-                        v = 0x7FFFFFFFu - gid[q];
-                        return key[q] == tie_key;
-                    };
-                    if (!block_radix_level<QK>(sm, kf, gw, gspan, gs, need, gbin, gcb)) {
-                        gopen = false;
-                    } else {
-                        gw += gbin << gs;
-                        if ((int)gcb == need || gs == 0) {
-                            gopen = false;
-                        } else {
-                            gspan = (1u << gs) - 1u;
-                            gs = gs > 8 ? gs - 8 : 0u;
-                        }
-                    }
-                }
-            }
-            if (ties && ntie > (uint32_t)kWave) gid_cut = 0x7FFFFFFFu - gw;
-        }
-    }
-
-    // Emission in candidate order.
-    fresh();
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int q = 0; q < QK; ++q) {
-        const bool sel = key[q] != 0u && (key[q] > thr_gt || (key[q] == tie_key && gid[q] <= gid_cut));
-        cnt += (uint32_t)__popcll(__ballot(sel));
-    }
-    if (lane == 0) sm.red[wave][3] = cnt;
-    __syncthreads();
-    uint32_t base = 0, total = 0;
-    for (int w = 0; w < world; ++w) {
-        const uint32_t c = sm.red[w][3];
-        base += w < wave ? c : 0u;
-        total += c;
-    }
     int32_t* o_row = out_ids + row * (int64_t)k;
+    // The row re-read from memory (cached) for the rare paths, so that no
+    // candidate registers are held across their barriers.
+    auto visit_mem = [&](auto f) __attribute__((always_inline)) {
+        constexpr int QC = QK < 8 ? QK : 8;  // registers per step
+#pragma unroll 1
+        for (int q0 = 0; q0 < QK; q0 += QC) {
+#pragma unroll
+            for (int q = 0; q < QC; ++q) {
+                const int j = (q0 + q) * kWave + lane;
+                const i32x2 v = src[j < kc ? j : 0];
+                const uint32_t u = (uint32_t)v[0];
+                const bool valid = j < kc && v[1] >= 0 && !f32_bits_is_nan(u);
+                f(valid ? key32_of_bits(u) : 0u, (uint32_t)v[1]);
+            }
+        }
+    };
+
+    if (nv <= (uint32_t)k) {  // every valid candidate is selected
+        pair_emit_visit(sm, visit_mem, PairCut{0u, 0u, 0u}, world, k, o_row);
+        return;
+    }
+
+    // First level on the registers.
+    const uint32_t span0 = mx - mn;
+    const int bl = span0 ? 32 - __clz((int)span0) : 0;
+    const uint32_t sh0 = bl > 8 ? (uint32_t)(bl - 8) : 0u;
+    int need = k;
     fresh();
 #pragma unroll
-    for (int q = 0; q < QK; ++q) {
-        const bool sel = key[q] != 0u && (key[q] > thr_gt || (key[q] == tie_key && gid[q] <= gid_cut));
-        const uint64_t m = __ballot(sel);
-        const uint32_t pos = base + mbcnt64(m);
-        if (sel && pos < (uint32_t)k) o_row[pos] = (int32_t)gid[q];
-        base += (uint32_t)__popcll(m);
+    for (int q = 0; q < QK; ++q) pair_hist_add(sm, key[q], mn, span0, sh0);
+    uint32_t bin, cb;
+    const bool ok = pair_hist_find(sm, need, bin, cb);
+    const uint32_t blo = mn + (bin << sh0);
+    const uint32_t nlist = (uint32_t)(k - need) + cb;  // keys >= blo
+
+    if (ok && nlist <= (uint32_t)kPairListCap) {
+        // Compact the keys >= blo into the list, in candidate order.
+        uint32_t c = 0;
+        fresh();
+#pragma unroll
+        for (int q = 0; q < QK; ++q) c += (uint32_t)__popcll(__ballot(key[q] >= blo));
+        if (lane == 0) sm.woff[wave] = c;
+        lds_barrier();
+        uint32_t off = 0;
+        for (int w = 0; w < wave; ++w) off += sm.woff[w];
+        fresh();
+#pragma unroll
+        for (int q = 0; q < QK; ++q) {
+            const bool in = key[q] >= blo;
+            const uint64_t m = __ballot(in);
+            const uint32_t p = off + mbcnt64(m);
+            if (in && p < (uint32_t)kPairListCap) {
+                sm.lkey[p] = key[q];
+                sm.lgid[p] = (uint32_t)src[q * kWave + lane][1];  // cached: the row was just read
+            }
+            off += (uint32_t)__popcll(m);
+        }
+        lds_barrier();
+
+        auto visit_list = [&](auto f) __attribute__((always_inline)) {
+#pragma unroll 1
+            for (int i = threadIdx.x; i < (int)nlist; i += nthreads) f(sm.lkey[i], sm.lgid[i]);
+        };
+        PairCut cut{blo - 1u, 0u, 0u};
+        if ((int)cb != need) {
+            bool ties;
+            uint32_t ntie;
+            if (sh0 == 0) {
+                ties = true;
+                cut.thr_gt = blo;
+                cut.tie_key = blo;
+                ntie = cb;
+            } else {
+                const uint32_t top = mx - blo, width1 = (1u << sh0) - 1u;
+                pair_levels(sm, visit_list, need, blo, width1 < top ? width1 : top,
+                            sh0 > 8 ? sh0 - 8 : 0u, mx, cut.thr_gt, ties, cut.tie_key, ntie);
+            }
+            if (ties) cut.gid_cut = pair_tie_cut(sm, visit_list, cut.tie_key, ntie, need);
+        }
+        pair_emit_list(sm, cut, world, k, o_row);
+    } else {
+        // Rare (heavy ties, or a boundary bin too full for the list):
+        // levels from the full window over the row re-read from memory.
+        need = k;
+        PairCut cut{0u, 0u, 0u};
+        bool ties;
+        uint32_t ntie;
+        pair_levels(sm, visit_mem, need, mn, span0, sh0, mx, cut.thr_gt, ties, cut.tie_key, ntie);
+        if (ties) cut.gid_cut = pair_tie_cut(sm, visit_mem, cut.tie_key, ntie, need);
+        pair_emit_visit(sm, visit_mem, cut, world, k, o_row);
     }
-    for (int p = (int)(total < (uint32_t)k ? total : (uint32_t)k) + (int)threadIdx.x; p < k; p += nthreads)
-        o_row[p] = -1;
 }
 
 template <int KPT>

@@ -155,6 +155,33 @@ def test_pairs_random(rts):
         assert_ids_equal(got, exp, f"pairs {world} {kc} {k}")
 
 
+@pytest.mark.parametrize("regime", ["all_equal", "eight_values", "quantized", "few_valid"])
+def test_pairs_tie_regimes(rts, regime):
+    # Score ties that fall on the k-th key in every regime the select handles
+    # differently: a tie set of up to 64, a larger one, a boundary bin too full
+    # for the LDS list (all scores equal), and rows with at most k valid.
+    rng = np.random.default_rng(77)
+    for world, kc, k in ((8, 2048, 2048), (4, 512, 512), (3, 100, 64)):
+        rows = 12
+        if regime == "all_equal":
+            v = np.full((world, rows, kc), 0.75, np.float32)
+        elif regime == "eight_values":
+            v = rng.integers(0, 8, (world, rows, kc)).astype(np.float32)
+        elif regime == "quantized":
+            v = (np.round(rng.standard_normal((world, rows, kc)) * 300) / 300).astype(np.float32)
+        else:
+            v = rng.standard_normal((world, rows, kc)).astype(np.float32)
+        p = np.zeros((world, rows, kc, 2), np.int32)
+        p[..., 0] = v.view(np.int32)
+        p[..., 1] = np.stack([rng.permutation(1 << 20)[:kc * world].reshape(world, kc)
+                              for _ in range(rows)], axis=1)
+        if regime == "few_valid":
+            p[..., 1][rng.random(v.shape) < 1.0 - 0.8 * k / (world * kc)] = -1
+        say("pairs ties", regime, world, kc, k)
+        got = host(rts.merge_select_pairs_rank_major(dev(p), k))
+        assert_ids_equal(got, oracle.merge_select_pairs_rank_major(p, k), f"pairs {regime} {world} {kc} {k}")
+
+
 def test_pack_pairs_random(rts):
     rng = np.random.default_rng(31)
     rows, cols, kc = 50, 5000, 256
