@@ -915,7 +915,7 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kPairCopies = 8;
 constexpr int kPairStride = 257;
-constexpr int kPairListCap = 4096;
+constexpr int kPairListCap = 3072;
 
 struct PairSmem {
     uint32_t hist[kPairCopies][kPairStride];
@@ -1147,7 +1147,7 @@ __device__ __forceinline__ void pair_emit_list(PairSmem& sm, const PairCut& c, i
 }
 
 template <int QK>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void merge_pairs_wave_kernel(
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void merge_pairs_wave_kernel(
     const int32_t* __restrict__ pairs, Layout lay, int32_t world, int64_t rows, int32_t kc,
     int32_t k, int32_t* __restrict__ out_ids) {
     __shared__ PairSmem sm;
