@@ -132,14 +132,6 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Workgroup barrier that orders LDS traffic only: vector-memory loads issued
-// before it stay in flight across it (a plain __syncthreads waits for them).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // ---------------------------------------------------------------------------
 // Bitonic network over 64*N values held "blocked" by one wave: lane l holds
 // elements l*N .. l*N+N-1 in v[0..N-1].  Partners closer than N are in the

@@ -913,6 +913,14 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
 // ties), runs the same levels, tie rule and emission over the row re-read
 // from memory, so that no candidate registers are held across them.
 // ---------------------------------------------------------------------------
+// Workgroup barrier that orders LDS traffic only (a plain __syncthreads also
+// waits for every outstanding vector-memory access of the wave).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 constexpr int kPairCopies = 8;
 constexpr int kPairStride = 257;
 constexpr int kPairListCap = 3072;
