@@ -24,6 +24,7 @@
 // addresses and banks.  Selected ids are written in candidate order (rank,
 // then slot), a fixed order that does not depend on the launch geometry.
 #include "rts_device.hpp"
+#include "rts_levels.hpp"
 #include "rts_internal.h"
 #include "../../include/row_top_select.h"
 
@@ -913,20 +914,10 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
 // ties), runs the same levels, tie rule and emission over the row re-read
 // from memory, so that no candidate registers are held across them.
 // ---------------------------------------------------------------------------
-// Workgroup barrier that orders LDS traffic only (a plain __syncthreads also
-// waits for every outstanding vector-memory access of the wave).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-constexpr int kPairCopies = 8;
-constexpr int kPairStride = 257;
 constexpr int kPairListCap = 3072;
 
 struct PairSmem {
-    uint32_t hist[kPairCopies][kPairStride];
+    uint32_t hist[kLevelCopies][kLevelStride];
     uint32_t bins[256];
     uint32_t red[16][4];
     uint32_t bc[4];
@@ -945,139 +936,6 @@ struct PairCut {
 
 __device__ __forceinline__ bool pair_selected(uint32_t key, uint32_t gid, const PairCut& c) {
     return key != 0u && (key > c.thr_gt || (key == c.tie_key && gid <= c.gid_cut));
-}
-
-// Counts key - wlo, when it lies in [0, span], into bin (key - wlo) >> sh.
-__device__ __forceinline__ void pair_hist_add(PairSmem& sm, uint32_t key, uint32_t wlo,
-                                              uint32_t span, uint32_t sh) {
-    const uint32_t x = key - wlo;
-    if (x <= span)
-        __hip_atomic_fetch_add(&sm.hist[lane_id() & (kPairCopies - 1)][x >> sh], 1u,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// All threads, after their pair_hist_add calls: sums (and clears) the copies,
-// then wave 0 finds the bin where the count from the top reaches need.
-// Returns (uniform) ok, the bin and its count, and lowers need by the count
-// above the bin.
-__device__ __forceinline__ bool pair_hist_find(PairSmem& sm, int& need, uint32_t& bin, uint32_t& cb) {
-    const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
-    lds_barrier();
-    for (int b = threadIdx.x; b < 256; b += blockDim.x) {  // the block may have < 256 threads
-        uint32_t t = 0;
-#pragma unroll
-        for (int c = 0; c < kPairCopies; ++c) {
-            t += sm.hist[c][b];
-            sm.hist[c][b] = 0u;  // clear for the next level
-        }
-        sm.bins[b] = t;
-    }
-    lds_barrier();
-    if (wave == 0) {
-        int nd = need;
-        uint32_t b, c;
-        const bool ok = radix_find(sm.bins, nd, b, c);
-        if (lane == 0) {
-            sm.bc[0] = ok ? 1u : 0u;
-            sm.bc[1] = b;
-            sm.bc[2] = c;
-            sm.bc[3] = (uint32_t)nd;
-        }
-    }
-    lds_barrier();
-    const bool ok = sm.bc[0] != 0u;
-    bin = sm.bc[1];
-    cb = sm.bc[2];
-    if (ok) need = (int)sm.bc[3];
-    lds_barrier();  // sm.bc is rewritten by the next level
-    return ok;
-}
-
-// Radix levels over the keys that `visit` hands out (visit(f) calls
-// f(key, gid) for each of this thread's entries), starting from the window
-// [wlo, wlo + span] in bins of 2^sh: ends with either a plain threshold (the
-// k selected are the keys > thr_gt) or ties at tie_key, ntie of them, of which
-// the `need` lowest gids are selected.
-template <typename Visit>
-__device__ __forceinline__ void pair_levels(PairSmem& sm, Visit visit, int& need, uint32_t wlo,
-                                            uint32_t span, uint32_t sh, uint32_t mx, uint32_t& thr_gt,
-                                            bool& ties, uint32_t& tie_key, uint32_t& ntie) {
-    ties = false;
-    tie_key = 0u;
-    ntie = 0u;
-    thr_gt = wlo - 1u;
-#pragma unroll 1
-    for (int level = 0; level < 4; ++level) {  // a 32-bit key needs four at most
-        visit([&](uint32_t key, uint32_t) __attribute__((always_inline)) { pair_hist_add(sm, key, wlo, span, sh); });
-        uint32_t bin, cb;
-        if (!pair_hist_find(sm, need, bin, cb)) {
-            thr_gt = wlo - 1u;
-            return;
-        }
-        const uint32_t blo = wlo + (bin << sh);
-        if ((int)cb == need) {
-            thr_gt = blo - 1u;
-            return;
-        }
-        if (sh == 0) {
-            thr_gt = blo;
-            tie_key = blo;
-            ties = true;
-            ntie = cb;
-            return;
-        }
-        wlo = blo;
-        const uint32_t top = mx - blo, width1 = (1u << sh) - 1u;
-        span = width1 < top ? width1 : top;
-        sh = sh > 8 ? sh - 8 : 0u;
-    }
-}
-
-// The largest gid taken among the ntie entries with key == tie_key, when the
-// `need` lowest gids are taken: a wave sort for up to 64, else levels over
-// 2^31 - 1 - gid.
-template <typename Visit>
-__device__ __forceinline__ uint32_t pair_tie_cut(PairSmem& sm, Visit visit, uint32_t tie_key,
-                                                 uint32_t ntie, int need) {
-    const int lane = lane_id();
-    if (ntie <= (uint32_t)kWave) {
-        visit([&](uint32_t key, uint32_t gid) __attribute__((always_inline)) {
-            if (key == tie_key) {
-                const uint32_t s = __hip_atomic_fetch_add(&sm.ntied, 1u, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_WORKGROUP);
-                if (s < (uint32_t)kWave) sm.tied[s] = gid;
-            }
-        });
-        lds_barrier();
-        if (threadIdx.x < (unsigned)kWave) {
-            uint64_t sv[1] = {lane < (int)ntie ? (uint64_t)sm.tied[lane] : ~0ull};
-            wave_bitonic_sort<1, false>(sv);
-            const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sv[0], need - 1);
-            if (lane == 0) {
-                sm.bc[0] = c;
-                sm.ntied = 0u;
-            }
-        }
-        lds_barrier();
-        const uint32_t cut = sm.bc[0];
-        lds_barrier();
-        return cut;
-    }
-    uint32_t gw = 0u, gspan = 0x7FFFFFFFu, gs = 23u;
-#pragma unroll 1
-    for (int gl = 0; gl < 4; ++gl) {
-        visit([&](uint32_t key, uint32_t gid) __attribute__((always_inline)) {
-            if (key == tie_key) pair_hist_add(sm, 0x7FFFFFFFu - gid, gw, gspan, gs);
-        });
-        uint32_t gbin, gcb;
-        if (!pair_hist_find(sm, need, gbin, gcb)) break;
-        gw += gbin << gs;
-        if ((int)gcb == need || gs == 0) break;
-        gspan = (1u << gs) - 1u;
-        gs = gs > 8 ? gs - 8 : 0u;
-    }
-    return 0x7FFFFFFFu - gw;
 }
 
 // Emission in candidate order from a visitor that hands out this lane's
@@ -1164,7 +1022,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     const int wave = threadIdx.x / kWave;  // the rank
     const int nthreads = kWave * world;
 
-    for (int q = threadIdx.x; q < kPairCopies * kPairStride; q += nthreads) (&sm.hist[0][0])[q] = 0u;
+    for (int q = threadIdx.x; q < kLevelCopies * kLevelStride; q += nthreads) (&sm.hist[0][0])[q] = 0u;
     if (threadIdx.x == 0) sm.ntied = 0u;
 
     const int64_t row = blockIdx.x;
@@ -1238,9 +1096,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     int need = k;
     fresh();
 #pragma unroll
-    for (int q = 0; q < QK; ++q) pair_hist_add(sm, key[q], mn, span0, sh0);
+    for (int q = 0; q < QK; ++q) level_hist_add(sm, key[q], mn, span0, sh0);
     uint32_t bin, cb;
-    const bool ok = pair_hist_find(sm, need, bin, cb);
+    const bool ok = level_hist_find(sm, need, bin, cb);
     const uint32_t blo = mn + (bin << sh0);
     const uint32_t nlist = (uint32_t)(k - need) + cb;  // keys >= blo
 
@@ -1283,10 +1141,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
                 ntie = cb;
             } else {
                 const uint32_t top = mx - blo, width1 = (1u << sh0) - 1u;
-                pair_levels(sm, visit_list, need, blo, width1 < top ? width1 : top,
+                radix_levels(sm, visit_list, need, blo, width1 < top ? width1 : top,
                             sh0 > 8 ? sh0 - 8 : 0u, mx, cut.thr_gt, ties, cut.tie_key, ntie);
             }
-            if (ties) cut.gid_cut = pair_tie_cut(sm, visit_list, cut.tie_key, ntie, need);
+            if (ties) cut.gid_cut = tie_cut(sm, visit_list, cut.tie_key, ntie, need);
         }
         pair_emit_list(sm, cut, world, k, o_row);
     } else {
@@ -1296,8 +1154,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
         PairCut cut{0u, 0u, 0u};
         bool ties;
         uint32_t ntie;
-        pair_levels(sm, visit_mem, need, mn, span0, sh0, mx, cut.thr_gt, ties, cut.tie_key, ntie);
-        if (ties) cut.gid_cut = pair_tie_cut(sm, visit_mem, cut.tie_key, ntie, need);
+        radix_levels(sm, visit_mem, need, mn, span0, sh0, mx, cut.thr_gt, ties, cut.tie_key, ntie);
+        if (ties) cut.gid_cut = tie_cut(sm, visit_mem, cut.tie_key, ntie, need);
         pair_emit_visit(sm, visit_mem, cut, world, k, o_row);
     }
 }
