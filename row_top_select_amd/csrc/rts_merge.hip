@@ -1112,17 +1112,31 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
         lds_barrier();
         uint32_t off = 0;
         for (int w = 0; w < wave; ++w) off += sm.woff[w];
+        // The listed entries' gids are read back from memory (mostly cached:
+        // the row was just read), a batch of registers' loads in flight
+        // together rather than one round trip per register.
+        constexpr int QB = QK < 8 ? QK : 8;
         fresh();
 #pragma unroll
-        for (int q = 0; q < QK; ++q) {
-            const bool in = key[q] >= blo;
-            const uint64_t m = __ballot(in);
-            const uint32_t p = off + mbcnt64(m);
-            if (in && p < (uint32_t)kPairListCap) {
-                sm.lkey[p] = key[q];
-                sm.lgid[p] = (uint32_t)src[q * kWave + lane][1];  // cached: the row was just read
+        for (int qb = 0; qb < QK; qb += QB) {
+            uint32_t g[QB];
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                const int q = qb + b;
+                g[b] = key[q] >= blo ? (uint32_t)src[q * kWave + lane][1] : 0u;
             }
-            off += (uint32_t)__popcll(m);
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                const int q = qb + b;
+                const bool in = key[q] >= blo;
+                const uint64_t m = __ballot(in);
+                const uint32_t p = off + mbcnt64(m);
+                if (in && p < (uint32_t)kPairListCap) {
+                    sm.lkey[p] = key[q];
+                    sm.lgid[p] = g[b];
+                }
+                off += (uint32_t)__popcll(m);
+            }
         }
         lds_barrier();
 
