@@ -1027,14 +1027,27 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
 
     const int64_t row = blockIdx.x;
     const i32x2* src = reinterpret_cast<const i32x2*>(pairs) + lay.at(wave, row) * kc;
+    // Pairs are loaded a batch of 8 registers at a time, all of a batch in
+    // flight together (left to itself the compiler waits after every load).
     uint32_t key[QK];
+    {
+        constexpr int QL = QK < 8 ? QK : 8;
 #pragma unroll
-    for (int q = 0; q < QK; ++q) {
-        const int j = q * kWave + lane;
-        const i32x2 pr = src[j < kc ? j : 0];  // QK may exceed ceil(kc / 64)
-        const uint32_t u = (uint32_t)pr[0];
-        const bool valid = j < kc && pr[1] >= 0 && !f32_bits_is_nan(u);
-        key[q] = valid ? key32_of_bits(u) : 0u;
+        for (int qb = 0; qb < QK; qb += QL) {
+            i32x2 pr[QL];
+#pragma unroll
+            for (int b = 0; b < QL; ++b) {
+                const int j = (qb + b) * kWave + lane;
+                pr[b] = src[j < kc ? j : 0];  // QK may exceed ceil(kc / 64)
+            }
+#pragma unroll
+            for (int b = 0; b < QL; ++b) {
+                const int j = (qb + b) * kWave + lane;
+                const uint32_t u = (uint32_t)pr[b][0];
+                const bool valid = j < kc && pr[b][1] >= 0 && !f32_bits_is_nan(u);
+                key[qb + b] = valid ? key32_of_bits(u) : 0u;
+            }
+        }
     }
     auto fresh = [&]() __attribute__((always_inline)) {
 #pragma unroll
