@@ -486,34 +486,56 @@ __device__ __forceinline__ void rescue_one_row(const int32_t* __restrict__ gathe
     const uint32_t r1 = (uint32_t)(world * n);
     const uint32_t total = r1 + (uint32_t)nsat * (uint32_t)k;
 
+    // Candidate words and their plane words are loaded a batch of KB
+    // registers at a time, every load of a batch in flight before the first
+    // is used (the plane load does not wait for the word's test).
+    constexpr int KB = KPT < 8 ? KPT : 8;
     uint64_t key[KPT];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        key[i] = 0ull;
-        const uint32_t f = (uint32_t)(i * kSelBlock + t);
-        if (f < r1) {
-            const uint32_t r = f / (uint32_t)n, j = f - r * (uint32_t)n;
-            if (!((mask >> r) & 1u)) {
-                const int32_t* rowp = gathered + ((int64_t)r * rows + row) * gw;
-                const uint32_t word = (uint32_t)rowp[j];
+    for (int ib = 0; ib < KPT; ib += KB) {
+        uint32_t wv[KB], pv[KB];
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            const uint32_t f = (uint32_t)((ib + b) * kSelBlock + t);
+            wv[b] = 0u;
+            pv[b] = 0u;
+            if (f < r1) {
+                const uint32_t r = f / (uint32_t)n, j = f - r * (uint32_t)n;
+                if (!((mask >> r) & 1u)) {
+                    const int32_t* rowp = gathered + ((int64_t)r * rows + row) * gw;
+                    wv[b] = (uint32_t)rowp[j];
+                    pv[b] = (uint32_t)rowp[n + (j >> 5)];
+                }
+            } else if (f < total) {
+                const uint32_t fr = f - r1, s = fr / (uint32_t)k, j = fr - s * (uint32_t)k;
+                const int32_t* slotp = recv + (row * slots + (int64_t)s) * pw;
+                wv[b] = (uint32_t)slotp[j];
+                pv[b] = (uint32_t)slotp[k + (j >> 5)];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            const int i = ib + b;
+            const uint32_t f = (uint32_t)(i * kSelBlock + t);
+            const uint32_t word = wv[b];
+            key[i] = 0ull;
+            if (f < r1) {
+                const uint32_t r = f / (uint32_t)n, j = f - r * (uint32_t)n;
+                // words of saturated ranks were not loaded (0)
                 if (word != 0u && (word >> 16) >= tau16) {
-                    const uint32_t plane = (uint32_t)rowp[n + (j >> 5)];
-                    const uint32_t local = (0xFFFFu - (word & 0xFFFFu)) | (((plane >> (j & 31)) & 1u) << 16);
+                    const uint32_t local = (0xFFFFu - (word & 0xFFFFu)) | (((pv[b] >> (j & 31)) & 1u) << 16);
                     key[i] = composite(word >> 16, local * (uint32_t)world + r);
                 }
-            }
-        } else if (f < total) {
-            const uint32_t fr = f - r1, s = fr / (uint32_t)k, j = fr - s * (uint32_t)k;
-            // owner: the s-th set bit of the mask
-            uint32_t m = mask;
-            for (uint32_t c = 0; c < s; ++c) m &= m - 1u;
-            const uint32_t owner = (uint32_t)__builtin_ctz(m);
-            const int32_t* slotp = recv + (row * slots + (int64_t)s) * pw;
-            const uint32_t word = (uint32_t)slotp[j];
-            if (word != 0u) {
-                const uint32_t plane = (uint32_t)slotp[k + (j >> 5)];
-                const uint32_t local = (0xFFFFu - (word & 0xFFFFu)) | (((plane >> (j & 31)) & 1u) << 16);
-                key[i] = composite(word >> 16, local * (uint32_t)world + owner);
+            } else if (f < total) {
+                const uint32_t fr = f - r1, s = fr / (uint32_t)k, j = fr - s * (uint32_t)k;
+                // owner: the s-th set bit of the mask
+                uint32_t m = mask;
+                for (uint32_t c = 0; c < s; ++c) m &= m - 1u;
+                const uint32_t owner = (uint32_t)__builtin_ctz(m);
+                if (word != 0u) {
+                    const uint32_t local = (0xFFFFu - (word & 0xFFFFu)) | (((pv[b] >> (j & 31)) & 1u) << 16);
+                    key[i] = composite(word >> 16, local * (uint32_t)world + owner);
+                }
             }
         }
     }
