@@ -136,7 +136,8 @@ def test_merge_packed_duplicates_stay_in_bounds(rts):
 
 def test_pairs_random(rts):
     rng = np.random.default_rng(21)
-    for world, kc, k in ((8, 2048, 2048), (4, 512, 512), (3, 100, 64), (2, 64, 1000)):
+    for world, kc, k in ((8, 2048, 2048), (4, 512, 512), (3, 100, 64), (2, 64, 1000), (16, 256, 1024),
+                         (16, 2048, 2048), (1, 2048, 512), (5, 1000, 2048)):
         rows = 30
         p = np.zeros((world, rows, kc, 2), np.int32)
         v = rng.standard_normal((world, rows, kc)).astype(np.float32)
