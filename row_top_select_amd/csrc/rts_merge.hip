@@ -14,9 +14,12 @@
 //     buffer read in place (PR 65178 Overview and Details).
 // The packed select runs one wave per row when a row's candidates fit in 64
 // registers per lane and world is a power of two up to 16
-// (merge_packed_wave_kernel); otherwise, and for pairs,
-// one 512-thread workgroup per row holds every candidate in registers as a
-// 64-bit composite (key << 32) | (0xFFFFFFFF - gid).  The k-th
+// (merge_packed_wave_kernel).  The pair select runs one wave per rank of a
+// row, with one radix level on the registers and the rest on an LDS list of
+// the boundary bin and above (merge_pairs_wave_kernel, up to 2048 pairs per
+// rank).  Otherwise (and for the second round) one 512-thread workgroup per
+// row holds every candidate in registers as a 64-bit composite
+// (key << 32) | (0xFFFFFFFF - gid).  The k-th
 // composite is found by a radix select whose 256 bins at each level span
 // [min, max] of the composites still in play (so a narrow score range still
 // spreads over the bins); histogram atomics go to 16 lane-striped LDS copies
