@@ -1044,7 +1044,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     __shared__ PairSmem sm;
     typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
     const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;  // the rank
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // the rank (uniform)
     const int nthreads = kWave * world;
 
     for (int q = threadIdx.x; q < kLevelCopies * kLevelStride; q += nthreads) (&sm.hist[0][0])[q] = 0u;
