@@ -1069,7 +1069,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
             for (int b = 0; b < QL; ++b) {
                 const int j = (qb + b) * kWave + lane;
                 const uint32_t u = (uint32_t)pr[b][0];
-                const bool valid = j < kc && pr[b][1] >= 0 && !f32_bits_is_nan(u);
+                const bool valid = j < kc && pr[b][1] >= 0 && !__builtin_isnan(__uint_as_float(u));
                 key[qb + b] = valid ? key32_of_bits(u) : 0u;
             }
         }
@@ -1080,12 +1080,15 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     };
 
     // Valid count and key range (every valid key is >= key32(-inf) > 0).
+    // The minimum is taken over key - 1, which sends empty slots (0) to the
+    // top of the unsigned range.
     uint32_t nv = 0, mn = 0xFFFFFFFFu, mx = 0u;
     fresh();
 #pragma unroll
     for (int q = 0; q < QK; ++q) {
         nv += (uint32_t)__popcll(__ballot(key[q] != 0u));
-        mn = (key[q] != 0u && key[q] < mn) ? key[q] : mn;
+        const uint32_t km1 = key[q] - 1u;
+        mn = km1 < mn ? km1 : mn;
         mx = key[q] > mx ? key[q] : mx;
     }
     mn = wave_min32(mn);
@@ -1104,6 +1107,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
         mn = sm.red[w][1] < mn ? sm.red[w][1] : mn;
         mx = sm.red[w][2] > mx ? sm.red[w][2] : mx;
     }
+    mn += 1u;  // the smallest valid key (used only when there are more than k)
     int32_t* o_row = out_ids + row * (int64_t)k;
     // The row re-read from memory (cached) for the rare paths, so that no
     // candidate registers are held across their barriers.
