@@ -37,6 +37,11 @@ KERNEL_SOURCES = ["row_top_select_amd/csrc/rts_topk_rows.hip",
                   "row_top_select_amd/csrc/rts_device.hpp"]
 
 
+def log(*a):
+    """Progress on stderr (the JSON line alone goes to stdout)."""
+    print(*a, file=sys.stderr, flush=True)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -50,24 +55,77 @@ def algorithmic_bytes(ends, k, rows, elem=4) -> int:
     return int(ends.astype("int64").sum()) * elem + rows * 4 + rows * k * 4
 
 
-def time_calls(fn, steps, warmup, torch):
+def time_calls(fn, steps, warmup, torch, per_call=None):
+    """Wall time of `steps` back-to-back calls after `warmup`, and the mean
+    per-call time from HIP events on the launch stream.  With a list as
+    `per_call`, an event is recorded between consecutive calls too (the calls
+    stay back to back) and each call's own time is appended to it."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True)
+           for _ in range(steps + 1 if per_call is not None else 2)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(steps):
+    evs[0].record(stream)
+    for i in range(steps):
         fn()
-    ev1.record(stream)
+        if per_call is not None:
+            evs[i + 1].record(stream)
+    evs[-1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, ev0.elapsed_time(ev1) / 1e3 / steps
+    if per_call is not None:
+        per_call.extend(evs[i].elapsed_time(evs[i + 1]) / 1e3 for i in range(steps))
+    return wall, evs[0].elapsed_time(evs[-1]) / 1e3 / steps
+
+
+def spread(ts):
+    """Median, min, max and mean of per-call times, in microseconds."""
+    v = sorted(ts)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"median_us": med * 1e6, "min_us": v[0] * 1e6, "max_us": v[-1] * 1e6,
+            "mean_us": sum(v) / n * 1e6, "calls": n}
 
 
 _SCRUB = None
+
+
+def time_cold_graph(fn, torch, rounds=4, calls=20, warmup=25):
+    """Per-call times of one call captured in a HIP graph and replayed with the
+    caches cold: before each replay a 1 GiB read-modify-write (larger than L2
+    and the 256 MB Infinity Cache) runs on the same stream, outside the two
+    events around the replay.  `warmup` replays, then `rounds` x `calls` timed."""
+    global _SCRUB
+    if _SCRUB is None:
+        _SCRUB = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(rounds):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(calls)]
+        for e0, e1 in evs:
+            _SCRUB.add_(1.0)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ts.extend(e0.elapsed_time(e1) / 1e3 for e0, e1 in evs)
+    del g
+    return ts
 
 
 def time_cold(fn, calls, torch):
@@ -143,28 +201,62 @@ def cpu_baseline(x_sample, ends_sample, k, total_rows_note):
         "cores": oracle.max_threads(),
         "kind": "oracle",
         "sample": f"{what} of the same workload (same data and row ends), one run, {dt:.2f} s wall; "
-                  f"host CPU {cpu_model()}",
+                  f"host CPU {cpu_model()}; the plain full-sort oracle (each row's valid entries "
+                  f"sorted with qsort, C -O2, OpenMP over rows), not a tuned CPU selector",
     }
 
 
+def _median_runs(fn, runs=3):
+    ts = []
+    for i in range(runs + 1):                 # the first run warms up
+        t0 = time.perf_counter()
+        fn()
+        if i:
+            ts.append(time.perf_counter() - t0)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
 def oracle_times(datagen):
-    """The oracle on tiny and prefill, on one thread and on all of them:
-    median of 3 timed runs after 1 warm-up (test infrastructure, CPU only)."""
+    """The oracle (test infrastructure, CPU only) on every workload, on all of
+    the host's threads (tiny and prefill also on one): wall-clock median of 3
+    runs after 1 warm-up.  For the merges it times the select alone, on the
+    oracle's own packed words and pairs of the merge workload."""
+    import numpy as np
     import oracle
-    res = {"cores": oracle.max_threads(), "cpu": cpu_model()}
-    for name in ("tiny", "prefill"):
+    cores = oracle.max_threads()
+    res = {"cores": cores, "cpu": cpu_model(), "workloads": {}}
+    for name in ("tiny", "prefill", "ties", "long", "decode", "robust", "robust_plus100",
+                 "robust_scale1e8"):
         w = datagen.WORKLOADS[name]
         x = datagen.logits(w, threads=8)
         ends = datagen.row_ends(w)
-        for threads in (1, oracle.max_threads()):
-            ts = []
-            for i in range(4):
-                t0 = time.perf_counter()
-                oracle.topk_rows(x, ends, w.k, nthreads=threads)
-                if i:
-                    ts.append(time.perf_counter() - t0)
-            ts.sort()
-            res[f"{name}_{threads}_threads_ms"] = ts[1] * 1e3
+        entry = {"shape": [w.rows, w.cols], "k": w.k}
+        for threads in ((1, cores) if name in ("tiny", "prefill") else (cores,)):
+            t = _median_runs(lambda: oracle.topk_rows(x, ends, w.k, nthreads=threads))
+            entry[f"ms_{threads}_threads"] = t * 1e3
+            entry[f"rows_per_s_{threads}_threads"] = w.rows / t
+        res["workloads"][name] = entry
+        log(f"oracle {name}: {entry}")
+        del x
+    W, N, K = datagen.MERGE_WORLD, datagen.MERGE_N, datagen.MERGE_K
+    ranks32 = datagen.rank_slices(datagen.merge_global(threads=8), W)
+    ranks16 = datagen.bf16_bits(ranks32)
+    packed = np.stack([oracle.pack_candidates(ranks16[r], oracle.topk_rows(ranks16[r], None, N))
+                       for r in range(W)])
+    del ranks16
+    t = _median_runs(lambda: oracle.merge_select_rank_major(packed, K))
+    res["workloads"]["merge_packed_select"] = {"shape": list(packed.shape), "k": K,
+                                               f"ms_{cores}_threads": t * 1e3,
+                                               f"rows_per_s_{cores}_threads": packed.shape[1] / t}
+    del packed
+    pairs = np.stack([oracle.pack_pairs(ranks32[r], oracle.topk_rows(ranks32[r], None, K), r, W)
+                      for r in range(W)])
+    del ranks32
+    t = _median_runs(lambda: oracle.merge_select_pairs_rank_major(pairs, K))
+    res["workloads"]["merge_pairs_select"] = {"shape": list(pairs.shape), "k": K,
+                                              f"ms_{cores}_threads": t * 1e3,
+                                              f"rows_per_s_{cores}_threads": pairs.shape[1] / t}
     return res
 
 
@@ -192,6 +284,7 @@ def secondary(torch, rts, datagen, steps, warmup):
         _, t = time_calls(call, steps, warmup, torch)
         t_cold = time_cold(call, 9, torch)
         b = algorithmic_bytes(ends_np, w.k, w.rows, elem=2 if bf16 else 4)
+        log(f"{name}: {t * 1e6:.1f} us warm, {t_cold * 1e6:.1f} us cold")
         res[name] = {"shape": [w.rows, w.cols], "k": w.k, "dtype": "bf16" if bf16 else "f32",
                      "us_per_call": t * 1e6, "rows_per_s": w.rows / t,
                      "algorithmic_GBps": b / t / 1e9, "cold_us_per_call": t_cold * 1e6,
@@ -249,6 +342,7 @@ def secondary(torch, rts, datagen, steps, warmup):
                         "select_plus_emit_rows_us": (t_sel + t_emit) * 1e6,
                         "fused_select_rows_us": t_fused * 1e6}
     del rows_out, valid
+    log(f"merge packed select {t_sel * 1e6:.1f} us, emit_rows {t_emit * 1e6:.1f} us")
     res["merge_packed"] = {"shape": [W, R, N + N // 32], "k": K,
                            "select_us": t_sel * 1e6, "select_rows_per_s": R / t_sel,
                            "select_algorithmic_GBps": sel_bytes / t_sel / 1e9,
@@ -281,6 +375,7 @@ def secondary(torch, rts, datagen, steps, warmup):
     _, t_resc = time_calls(lambda: rts.merge_rescue_rank_major(gathered, recv, sat, ids), steps,
                            warmup, torch)
     n_sat = int(((sat.cpu().numpy().view(np.uint32) >> 16) != 0).sum())
+    log(f"rescue {t_resc * 1e6:.1f} us")
     res["merge_rescue"] = {"shape": [W, R, N + N // 32], "recv": [R, slots, K + K // 32], "k": K,
                            "no_saturated_rows_us": t_fast * 1e6,
                            "rank_skewed_rows_saturated": n_sat,
@@ -305,6 +400,7 @@ def secondary(torch, rts, datagen, steps, warmup):
     pid_rm = torch.empty_like(pid)
     _, t_pairs_rm = time_calls(lambda: rts.merge_select_pairs_row_major(prm, K, W, out=pid_rm), steps,
                                warmup, torch)
+    log(f"pair select {t_pairs * 1e6:.1f} us")
     res["merge_pairs"] = {"shape": [W, R, K, 2], "k": K, "select_us": t_pairs * 1e6,
                           "select_rows_per_s": R / t_pairs,
                           "select_algorithmic_GBps": pb / t_pairs / 1e9,
@@ -412,7 +508,8 @@ def main():
     def step():
         rts.topk_rows(x, w.k, row_ends=ends, out=out, workspace=None)
 
-    wall, t_kernel = time_calls(step, args.steps, args.warmup, torch)
+    per_call = []
+    wall, t_kernel = time_calls(step, args.steps, args.warmup, torch, per_call=per_call)
     ms_per_step = wall / args.steps * 1e3
     value = w.rows * args.steps / wall
     abytes = algorithmic_bytes(ends_np, w.k, w.rows)
@@ -443,11 +540,18 @@ def main():
                    "cols": w.cols, "k": w.k, "row_ends": "98305+i", "distribution": "N(0,1)",
                    "seed": w.seed},
         "us_per_call": t_kernel * 1e6,
+        "per_call": spread(per_call),
         "achieved_GBps": achieved,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "algorithmic_bytes": abytes},
     }
+    # The pages' protocol: one call in a graph, replayed with cold caches
+    # (4 rounds x 20 calls after 25 warm-up replays); reported beside the
+    # warm back-to-back figures above, which `value` is.
+    cold = spread(time_cold_graph(step, torch))
+    cold["algorithmic_GBps_at_median"] = abytes / (cold["median_us"] * 1e-6) / 1e9
+    result["cold_graph_replay"] = cold
     if not args.no_cpu:
         # The whole workload is a few seconds of oracle time on the host's cores.
         ids, cpu = cpu_baseline(x_np, ends_np, w.k, w.rows)

@@ -22,27 +22,38 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+_LIB_PLAIN = os.path.join(_HERE, "liboracle.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same source, for
+# checking the oracle itself (tests/test_oracle_sanitized.py): loaded instead
+# of the plain one when ORACLE_SANITIZED=1, in a process started with the ASan
+# runtime preloaded.
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+SANITIZED = os.environ.get("ORACLE_SANITIZED") == "1"
+_LIB = _LIB_SAN if SANITIZED else _LIB_PLAIN
+_FLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra"]
+_SAN_FLAGS = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+              "-fno-sanitize-recover=undefined"]
 _lock = threading.Lock()
 _lib = None
 
 
-def build(force: bool = False) -> str:
-    """Compile ``oracle.c`` into ``liboracle.so`` (gcc, OpenMP over rows)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + f".tmp{os.getpid()}"
-        subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-             "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = False, sanitize: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` (gcc, OpenMP over rows), or
+    with ``sanitize`` into ``liboracle_san.so`` under ASan and UBSan."""
+    lib = _LIB_SAN if sanitize else _LIB_PLAIN
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", *_FLAGS, *(_SAN_FLAGS if sanitize else []),
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
+            build(sanitize=SANITIZED)
             lib = ctypes.CDLL(_LIB)
             i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
             lib.oracle_topk_rows.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i32, p, i64,

@@ -129,7 +129,11 @@ def topk_rows(logits: torch.Tensor, k: int, row_ends: torch.Tensor | None = None
         out = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
     if out.dtype != torch.int32:
         raise TypeError("out must be int32")
-    _, _, ld_out = _rows_ld(out, "out")
+    if out.device != logits.device:
+        raise ValueError("out must be on the device of logits")
+    out_rows, out_cols, ld_out = _rows_ld(out, "out")
+    if out_rows < rows or out_cols < k:
+        raise ValueError(f"out must hold at least [{rows}, {k}] (got {tuple(out.shape)})")
     if rows <= 1:
         ld_out = max(ld_out, k)
     ws, ws_bytes = None, 0
@@ -139,6 +143,9 @@ def topk_rows(logits: torch.Tensor, k: int, row_ends: torch.Tensor | None = None
             ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
             ws_bytes = need
     elif workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != logits.device or \
+                not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the device of logits")
         ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
     _check(_lib.topk_rows(_dev(logits, "logits"), dt, rows, cols, ld, _opt(row_ends, "row_ends"), k,
                           _dev(out, "out"), ld_out, _opt(ws, "workspace"), ws_bytes, _stream(stream)),

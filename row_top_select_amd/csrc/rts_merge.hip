@@ -258,6 +258,10 @@ __device__ void block_emit_rows(const uint64_t (&key)[KPT], uint64_t T, int32_t 
     const uint32_t total = block_excl_scan(v, excl, sm);
     if (t < KPT * kSelWaves) sm.tab[t] = excl;
     __syncthreads();
+    // With distinct composites at most k keys are >= T; repeated candidates
+    // (outside the contract) can select more, so every position is bounded
+    // by the row's out_cols.
+    const uint32_t cap = (uint32_t)ra.out_cols;
     int32_t* orow = ra.rows_out + row * (int64_t)ra.out_cols;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -266,11 +270,13 @@ __device__ void block_emit_rows(const uint64_t (&key)[KPT], uint64_t T, int32_t 
             const uint32_t local = gid / (uint32_t)world;
             int32_t phys = -1;
             owned_phys(ra, bt, local, phys);
-            orow[sm.tab[i * kSelWaves + wave] + mbcnt64(m[i])] = phys;
+            const uint32_t pos = sm.tab[i * kSelWaves + wave] + mbcnt64(m[i]);
+            if (pos < cap) orow[pos] = phys;
         }
     }
-    for (int p = (int)total + t; p < ra.out_cols; p += kSelBlock) orow[p] = -1;
-    if (t == 0) ra.valid_out[row] = (int32_t)total;
+    const uint32_t filled = total < cap ? total : cap;
+    for (int p = (int)filled + t; p < ra.out_cols; p += kSelBlock) orow[p] = -1;
+    if (t == 0) ra.valid_out[row] = (int32_t)filled;
     __syncthreads();  // sm.tab is reused by the caller
 }
 
@@ -908,8 +914,11 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
     if (o_row)
         for (int p = (base < k ? base : k) + lane; p < k; p += kWave) o_row[p] = -1;
     if (want_rows) {
-        for (int p = rbase + lane; p < ra.out_cols; p += kWave) r_row[p] = -1;
-        if (lane == 0) ra.valid_out[row] = rbase;
+        // rbase exceeds out_cols only with repeated candidates (outside the
+        // contract); the rows written stop at out_cols.
+        const int filled = rbase < ra.out_cols ? rbase : ra.out_cols;
+        for (int p = filled + lane; p < ra.out_cols; p += kWave) r_row[p] = -1;
+        if (lane == 0) ra.valid_out[row] = filled;
     }
     if (sat_word && lane == 0) {
         uint32_t mask = ~notsat & ((1u << world) - 1u);

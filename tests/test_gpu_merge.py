@@ -1,7 +1,7 @@
 """GPU parity of pack_candidates, merge_select_rank_major, pack_pairs and
 merge_select_pairs_rank_major against the CPU oracle (bit-exact ids, words and
-saturation words), on random and constructed inputs and on the merge workload
-(8 simulated ranks, 6710 rows) at full size with sampled oracle rows.
+saturation words), on random and constructed inputs.  The merge workload at
+full size is in test_gpu_merge_workload.py.
 
 Inputs of the merge selects are built by the oracle (or by hand), never by the
 GPU path."""
@@ -196,70 +196,6 @@ def test_pack_pairs_random(rts):
     assert np.array_equal(got, exp)
 
 
-def test_merge_workload_pipeline_sampled(rts):
-    # Global 6710 x 131072 N(0,1) logits; rank r owns columns g % 8 == r.  GPU:
-    # local top-384 (bf16) -> pack -> rank-major [8, 6710, 396] -> select top-2048.
-    # Pair variant: local top-2048 (fp32) -> pairs [8, 6710, 2048, 2] -> select.
-    W, R, S, N, K = (datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_LOCAL_COLS,
-                     datagen.MERGE_N, datagen.MERGE_K)
-    say("merge workload: generate")
-    g32 = datagen.merge_global()
-    ranks32 = datagen.rank_slices(g32, W)
-    del g32
-    ranks16 = datagen.bf16_bits(ranks32)
-    say("merge workload: gpu")
-    x16 = bf16_dev(ranks16)
-    gathered = torch.empty((W, R, N + N // 32), dtype=torch.int32, device="cuda")
-    locs = []
-    for r in range(W):
-        loc = rts.topk_rows(x16[r], N)
-        locs.append(loc)
-        rts.pack_candidates(x16[r], loc, out=gathered[r])
-    ids, sat = rts.merge_select_rank_major(gathered, K)
-    x32 = dev(ranks32)
-    pairs = torch.empty((W, R, K, 2), dtype=torch.int32, device="cuda")
-    for r in range(W):
-        loc2 = rts.topk_rows(x32[r], K)
-        rts.pack_pairs(x32[r], loc2, r, W, out=pairs[r])
-    pids = rts.merge_select_pairs_rank_major(pairs, K)
-    # The reordered (row-major) buffers select the same ids, bit for bit.
-    say("merge workload: row-major")
-    rm_ids, rm_sat = rts.merge_select_row_major(gathered.movedim(0, 1).contiguous(), K)
-    rm_pids = rts.merge_select_pairs_row_major(pairs.movedim(0, 1).reshape(R, W * K, 2).contiguous(),
-                                               K, W)
-    assert torch.equal(rm_ids, ids) and torch.equal(rm_sat, sat), "row-major packed select"
-    assert torch.equal(rm_pids, pids), "row-major pair select"
-    del rm_ids, rm_sat, rm_pids
-    ids, sat, pids = host(ids), host(sat), host(pids)
-    gpu_locs = np.stack([host(l) for l in locs])
-    gpu_packed = host(gathered)
-
-    sample = np.arange(0, R, 53)
-    say("merge workload: oracle on", len(sample), "rows")
-    o_packed = np.stack([oracle.pack_candidates(ranks16[r][sample],
-                                                oracle.topk_rows(ranks16[r][sample], None, N))
-                         for r in range(W)])
-    o_locs = np.stack([oracle.topk_rows(ranks16[r][sample], None, N) for r in range(W)])
-    assert_ids_equal(gpu_locs[:, sample].reshape(-1, N), o_locs.reshape(-1, N), "local top-384")
-    assert np.array_equal(gpu_packed[:, sample], o_packed), "packed words"
-    eids, esat = oracle.merge_select_rank_major(o_packed, K)
-    assert_ids_equal(ids[sample], eids, "merged ids")
-    assert np.array_equal(sat[sample], esat), "sat_word"
-    o_pairs = np.stack([oracle.pack_pairs(ranks32[r][sample],
-                                          oracle.topk_rows(ranks32[r][sample], None, K), r, W)
-                        for r in range(W)])
-    assert_ids_equal(pids[sample], oracle.merge_select_pairs_rank_major(o_pairs, K), "pair ids")
-    # Every row: with an empty mask the packed result is the exact bf16 top-K;
-    # the pair result is the exact fp32 top-K of the union (each rank sent its top-K).
-    assert ((sat.view(np.uint32) >> 16) == 0).mean() > 0.99
-    for t in sample[:8]:
-        row = np.empty(W * S, np.float32)
-        for r in range(W):
-            row[r::W] = ranks32[r, t]
-        direct = np.argsort(-row, kind="stable")[:K]
-        assert set(pids[t].tolist()) == set(direct.tolist())
-
-
 # ---------------------------------------------------------------------------
 # Second round (rescue) of the packed merge
 # ---------------------------------------------------------------------------
@@ -370,56 +306,6 @@ def test_rescue_limits(rts):
     assert (host(out2) == 9).all()
 
 
-def test_rescue_workload_pipeline_sampled(rts):
-    # Rank-skewed merge workload (6710 rows, 8 ranks, N = 384, K = 2048): round
-    # 1 on the GPU, every rank's local top-2048 packed and pushed, the rescue;
-    # sampled rows against the oracle's own pipeline, and the pages' exactness
-    # claim (selected scores = top-K of the union) on every sampled row.
-    W, R, S, N, K = (datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_LOCAL_COLS,
-                     datagen.MERGE_N, datagen.MERGE_K)
-    say("rescue workload: generate")
-    g32 = datagen.skew_ranks(datagen.merge_global())
-    ranks16 = datagen.bf16_bits(datagen.rank_slices(g32, W))
-    del g32
-    say("rescue workload: gpu")
-    x16 = bf16_dev(ranks16)
-    gathered = torch.empty((W, R, N + N // 32), dtype=torch.int32, device="cuda")
-    for r in range(W):
-        rts.pack_candidates(x16[r], rts.topk_rows(x16[r], N), out=gathered[r])
-    ids, sat = rts.merge_select_rank_major(gathered, K)
-    ids1 = host(ids).copy()
-    recv = torch.zeros((R, (K - 1) // N, K + K // 32), dtype=torch.int32, device="cuda")
-    local = torch.empty((R, K + K // 32), dtype=torch.int32, device="cuda")
-    for r in range(W):
-        rts.pack_candidates(x16[r], rts.topk_rows(x16[r], K), out=local)
-        rts.rescue_push(local, r, W, N, sat, recv)
-    rts.merge_rescue_rank_major(gathered, recv, sat, ids)
-    ids2, sat_h = host(ids), host(sat)
-    masks = sat_h.view(np.uint32) >> 16
-    assert ((masks != 0).mean() > 0.5), "the skewed workload should saturate most rows"
-    assert np.array_equal(ids2[masks == 0], ids1[masks == 0]), "rows with an empty mask changed"
-
-    sample = np.arange(3, R, 61)
-    say("rescue workload: oracle on", len(sample), "rows")
-    sub = ranks16[:, sample]
-    o_packed = np.stack([oracle.pack_candidates(sub[r], oracle.topk_rows(sub[r], None, N))
-                         for r in range(W)])
-    o_ids1, o_sat = oracle.merge_select_rank_major(o_packed, K)
-    assert np.array_equal(sat_h[sample], o_sat), "sat_word"
-    o_recv = np.zeros((len(sample), (K - 1) // N, K + K // 32), np.int32)
-    for r in range(W):
-        oracle.rescue_push(oracle.pack_candidates(sub[r], oracle.topk_rows(sub[r], None, K)), r, W, N,
-                           o_sat, o_recv)
-    o_ids2 = oracle.merge_rescue_rank_major(o_packed, o_recv, o_sat, o_ids1)
-    assert_ids_equal(ids2[sample], o_ids2, "rescued ids")
-    vals = datagen.bf16_to_f32(sub)                            # [W, rows, S]
-    for i in range(len(sample)):
-        row = np.empty(W * S, np.float32)
-        for r in range(W):
-            row[r::W] = vals[r, i]
-        assert np.array_equal(np.sort(row[ids2[sample[i]]]), np.sort(row)[-K:]), sample[i]
-
-
 # ---------------------------------------------------------------------------
 # emit_rows: a rank's owned physical KV rows
 # ---------------------------------------------------------------------------
@@ -462,44 +348,6 @@ def test_emit_rows_strided_table(rts):
     e_rows, e_valid = oracle.emit_rows(ids, world, 1, req, wide[:, :12], B, B)
     assert_ids_equal(host(rows_out), e_rows, "rows_out")
     assert np.array_equal(host(valid), e_valid)
-
-
-def test_emit_rows_merge_workload(rts):
-    # Merge workload (6710 rows, 8 ranks, top-2048): every rank's owned rows of
-    # the GPU select; sampled rows against the oracle's emit_rows of the
-    # oracle's own select, and over all rows the ranks partition the ids.
-    W, R, N, K = datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_N, datagen.MERGE_K
-    B, nreq, cols = 64, 97, 300                   # local ids < 16384 need 256 blocks of 64
-    rng = np.random.default_rng(77)
-    table = np.stack([rng.permutation(200000)[:cols] for _ in range(nreq)]).astype(np.int32)
-    req = (np.arange(R) % nreq).astype(np.int32)
-    table_short = np.ascontiguousarray(table[:, :200])   # local ids past 200 * 64 drop out
-    say("emit_rows workload: generate")
-    ranks16 = datagen.bf16_bits(datagen.rank_slices(datagen.merge_global(), W))
-    x16 = bf16_dev(ranks16)
-    gathered = torch.empty((W, R, N + N // 32), dtype=torch.int32, device="cuda")
-    for r in range(W):
-        rts.pack_candidates(x16[r], rts.topk_rows(x16[r], N), out=gathered[r])
-    ids, _ = rts.merge_select_rank_major(gathered, K)
-    del x16
-    sample = np.arange(5, R, 97)
-    sub = ranks16[:, sample]
-    o_packed = np.stack([oracle.pack_candidates(sub[r], oracle.topk_rows(sub[r], None, N))
-                         for r in range(W)])
-    o_ids, _ = oracle.merge_select_rank_major(o_packed, K)
-    req_d = dev(req)
-    for tab in (table, table_short):
-        tab_d = dev(tab)
-        total = torch.zeros(R, dtype=torch.int64, device="cuda")
-        for rank in range(W):
-            say("emit_rows workload rank", rank, tab.shape)
-            rows_out, valid = rts.emit_rows(ids, W, rank, req_d, tab_d, B, B)
-            total += valid.long()
-            e_rows, e_valid = oracle.emit_rows(o_ids, W, rank, req[sample], tab, B, B)
-            assert_ids_equal(host(rows_out)[sample], e_rows, "rows_out")
-            assert np.array_equal(host(valid)[sample], e_valid)
-        inside = (((ids // W) // B) < tab.shape[1]).sum(dim=1)
-        assert torch.equal(total, inside.long()), "ranks do not partition the selected ids"
 
 
 # ---------------------------------------------------------------------------
@@ -572,25 +420,46 @@ def test_merge_rescue_rows_fused(rts):
     assert entered
 
 
-def test_merge_rows_workload_all_ranks(rts):
-    # Merge workload: the fused select's rows equal emit_rows of the select's
-    # ids for every rank, over all 6710 rows.
-    W, R, N, K = datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_N, datagen.MERGE_K
-    rng = np.random.default_rng(5)
-    table = np.stack([rng.permutation(200000)[:256] for _ in range(97)]).astype(np.int32)
-    req = (np.arange(R) % 97).astype(np.int32)
-    say("fused rows workload: generate")
-    ranks16 = datagen.bf16_bits(datagen.rank_slices(datagen.merge_global(), W))
-    x16 = bf16_dev(ranks16)
-    del ranks16
-    gathered = torch.empty((W, R, N + N // 32), dtype=torch.int32, device="cuda")
-    for r in range(W):
-        rts.pack_candidates(x16[r], rts.topk_rows(x16[r], N), out=gathered[r])
-    del x16
-    ids, _ = rts.merge_select_rank_major(gathered, K)
-    req_d, tab_d = dev(req), dev(table)
-    for rank in range(W):
-        say("fused rows workload rank", rank)
-        two_rows, two_valid = rts.emit_rows(ids, W, rank, req_d, tab_d, 64, 64)
-        f_rows, f_valid, _, _ = rts.merge_select_rank_major_rows(gathered, K, rank, req_d, tab_d, 64, 64)
-        assert torch.equal(f_rows, two_rows) and torch.equal(f_valid, two_valid), rank
+@pytest.mark.parametrize("world,n,k,rescue", [(3, 96, 64, False), (8, 2048, 1024, False),
+                                              (3, 32, 64, True), (8, 64, 192, True)])
+def test_repeated_words_rows_stay_in_bounds(rts, world, n, k, rescue):
+    # Repeated words inside one rank (the same local id in many slots) are
+    # outside the contract: more than k candidates can tie with the k-th
+    # composite.  In round 1 (block kernel: world 3, or world * ceil(n/64) >
+    # 64) rank 0 then owns n > out_cols selected candidates; in the second
+    # round its receive slot holds k copies.  The fused rows outputs must stop
+    # at out_cols: the guard rows around rows_out and valid_out stay untouched.
+    rng = np.random.default_rng(world * 31 + n + k)
+    rows, B = 6, 16
+    g = _gathered(rng, world, rows, n, 1.0)
+    top = np.int32((0xFE00 << 16) | (0xFFFF - 5) - (1 << 32))   # a huge score, local id 5
+    g[0, :, :n] = top                              # rank 0: n copies of one candidate
+    g[0, :, n:] = 0
+    table = _table(rng, cols=(1 << 17) // B + 1)
+    req = rng.integers(0, table.shape[0], size=rows).astype(np.int32)
+    out_cols = k + 3
+    guard = 424242
+    buf = torch.full(((rows + 2) * out_cols,), guard, dtype=torch.int32, device="cuda")
+    rows_out = buf[out_cols:(rows + 1) * out_cols].view(rows, out_cols)
+    vbuf = torch.full((rows + 2,), guard, dtype=torch.int32, device="cuda")
+    valid = vbuf[1:rows + 1]
+    g_d, req_d, tab_d = dev(g), dev(req), dev(table)
+    say("repeated words rows", world, n, k, rescue)
+    if not rescue:
+        rts.merge_select_rank_major_rows(g_d, k, 0, req_d, tab_d, B, B, rows_out=rows_out,
+                                         valid_out=valid)
+    else:
+        slots = (k - 1) // n
+        recv = np.ascontiguousarray(_gathered(rng, slots, rows, k, 1.0).transpose(1, 0, 2))
+        recv[:, 0, :k] = top                       # slot 0 (owned by rank 0): k copies
+        recv[:, 0, k:] = 0
+        sw = np.full(rows, (1 << 16) | 0x7F00, np.uint32).view(np.int32)   # rank 0 saturated
+        rts.merge_rescue_rank_major_rows(g_d, dev(recv), dev(sw), k, 0, req_d, tab_d, B, B,
+                                         rows_out, valid)
+    b, v = host(buf).reshape(rows + 2, out_cols), host(vbuf)
+    assert (b[0] == guard).all() and (b[-1] == guard).all(), "rows_out written out of bounds"
+    assert v[0] == guard and v[-1] == guard, "valid_out written out of bounds"
+    assert ((v[1:-1] >= 0) & (v[1:-1] <= out_cols)).all()
+    # the first valid_out entries of each row are physical rows, then -1
+    for t in range(rows):
+        assert (b[t + 1, v[t + 1]:] == -1).all()
