@@ -19,7 +19,9 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is a DEVICE pointer owned by the caller; the
- *     library never allocates, frees or retains memory and keeps no state.
+ *     library never allocates, frees or retains memory and keeps no state,
+ *     except the static device scratch of topk_rows_noalloc (one array per
+ *     GPU, its address cached on the first call there).
  *   - Every call only validates its arguments on the host and enqueues work on
  *     `stream` (0 = the null stream); it never synchronises, so calls are
  *     stream-ordered and may be captured into a HIP graph.  Data the kernels
@@ -92,6 +94,29 @@ size_t topk_rows_workspace_size(int dtype, int64_t rows, int64_t cols, int32_t k
 int topk_rows(const void* logits, int dtype, int64_t rows, int64_t cols, int64_t ld_logits,
               const int32_t* row_ends, int32_t k, int32_t* out_idx, int64_t ld_out,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * topk_rows_noalloc -- topk_rows for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments (minus the workspace), outputs and
+ * errors as topk_rows, and the same result.
+ *
+ * Where topk_rows would split long rows of a small batch over several
+ * workgroups with a caller workspace, this call keeps the partial lists in a
+ * static device array of the library instead: 16 MiB (every launch plan of
+ * this library fits in it), one per GPU, held from the first call on that
+ * GPU until the process ends.  The array's address on the current device is
+ * taken on the first call there (make that first call outside graph
+ * capture); no call allocates or frees memory.  Nothing in the array needs
+ * clearing between calls: each launch writes every list it reads.  Calls on
+ * one GPU share its array, so two calls whose executions overlap on that GPU
+ * (different streams without ordering between them) race; calls ordered on
+ * one stream do not.  A plan that needed more than the array holds would be
+ * refused with RTS_EWORKSPACE.  `stream` must belong to the current device.
+ */
+int topk_rows_noalloc(const void* logits, int dtype, int64_t rows, int64_t cols, int64_t ld_logits,
+                      const int32_t* row_ends, int32_t k, int32_t* out_idx, int64_t ld_out,
+                      hipStream_t stream);
 
 /*
  * pack_candidates -- a rank's local top-n as B' words ([P2] module docstring

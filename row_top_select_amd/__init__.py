@@ -32,6 +32,7 @@ _lib.rts_status_string.restype = ctypes.c_char_p
 _lib.topk_rows_workspace_size.argtypes = [ctypes.c_int, _i64, _i64, _i32]
 _lib.topk_rows_workspace_size.restype = _sz
 _lib.topk_rows.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i32, _p, _i64, _p, _sz, _p]
+_lib.topk_rows_noalloc.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i32, _p, _i64, _p]
 _lib.pack_candidates.argtypes = [_p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p, _p]
 _lib.merge_select_rank_major.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p, _p]
 _lib.pack_pairs.argtypes = [_p, _i64, _i64, _i64, _p, _i32, _i64, _p, _i32, _i32, _p, _p]
@@ -44,7 +45,7 @@ _lib.merge_select_rank_major_rows.argtypes = [_p, _i32, _i64, _i32, _i32, _p, _p
 _lib.merge_rescue_rank_major_rows.argtypes = [_p, _p, _i32, _i64, _i32, _i32, _p, _p, _p, _p]
 _lib.rescue_push.argtypes = [_p, _i32, _i32, _i64, _i32, _i32, _p, _p, _p]
 _lib.merge_rescue_rank_major.argtypes = [_p, _p, _i32, _i64, _i32, _i32, _p, _p, _p]
-for _f in (_lib.topk_rows, _lib.pack_candidates, _lib.merge_select_rank_major, _lib.pack_pairs,
+for _f in (_lib.topk_rows, _lib.topk_rows_noalloc, _lib.pack_candidates, _lib.merge_select_rank_major, _lib.pack_pairs,
            _lib.merge_select_pairs_rank_major, _lib.rescue_push, _lib.merge_rescue_rank_major,
            _lib.merge_select_row_major, _lib.merge_select_pairs_row_major, _lib.emit_rows,
            _lib.merge_select_rank_major_rows, _lib.merge_rescue_rank_major_rows):
@@ -150,6 +151,33 @@ def topk_rows(logits: torch.Tensor, k: int, row_ends: torch.Tensor | None = None
     _check(_lib.topk_rows(_dev(logits, "logits"), dt, rows, cols, ld, _opt(row_ends, "row_ends"), k,
                           _dev(out, "out"), ld_out, _opt(ws, "workspace"), ws_bytes, _stream(stream)),
            "topk_rows")
+    return out
+
+
+def topk_rows_noalloc(logits: torch.Tensor, k: int, out: torch.Tensor,
+                      row_ends: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """topk_rows into a caller-given ``out`` with no allocation at all (split rows use
+    the library's static device scratch); see topk_rows_noalloc in the header."""
+    if logits.dtype == torch.float32:
+        dt = RTS_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = RTS_BF16
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    rows, cols, ld = _rows_ld(logits, "logits")
+    row_ends = _int32_vec(row_ends, rows, "row_ends")
+    if out.dtype != torch.int32:
+        raise TypeError("out must be int32")
+    if out.device != logits.device:
+        raise ValueError("out must be on the device of logits")
+    out_rows, out_cols, ld_out = _rows_ld(out, "out")
+    if out_rows < rows or out_cols < k:
+        raise ValueError(f"out must hold at least [{rows}, {k}] (got {tuple(out.shape)})")
+    if rows <= 1:
+        ld_out = max(ld_out, k)
+    _check(_lib.topk_rows_noalloc(_dev(logits, "logits"), dt, rows, cols, ld,
+                                  _opt(row_ends, "row_ends"), k, _dev(out, "out"), ld_out,
+                                  _stream(stream)), "topk_rows_noalloc")
     return out
 
 

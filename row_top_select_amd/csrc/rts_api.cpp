@@ -59,6 +59,31 @@ int topk_rows(const void* logits, int dtype, int64_t rows, int64_t cols, int64_t
                                  plan, workspace, stream);
 }
 
+int topk_rows_noalloc(const void* logits, int dtype, int64_t rows, int64_t cols, int64_t ld_logits,
+                      const int32_t* row_ends, int32_t k, int32_t* out_idx, int64_t ld_out,
+                      hipStream_t stream) {
+    if (dtype != RTS_F32 && dtype != RTS_BF16) return RTS_EINVAL;
+    if (rows < 0 || cols < 0 || ld_logits < cols || ld_logits < 0 || k < 1 || ld_out < k)
+        return RTS_EINVAL;
+    if (k > kMaxK || cols > 0x7FFFFFFFll) return RTS_EUNSUPPORTED;
+    if (rows == 0) return RTS_OK;
+    if (!out_idx || (cols > 0 && !logits)) return RTS_EINVAL;
+    const size_t esz = dtype == RTS_F32 ? 4 : 2;
+    if (!aligned(logits, esz) || !aligned(out_idx, 4) || (row_ends && !aligned(row_ends, 4)))
+        return RTS_EINVAL;
+    rts::TopkPlan plan = rts::plan_topk_rows(dtype, rows, cols, k, true);
+    void* scratch = nullptr;
+    if (plan.groups > 1) {
+        size_t bytes = 0;
+        const int rc = rts::scratch_of_current_device(&scratch, &bytes);
+        if (rc != RTS_OK) return rc;
+        if (plan.ws_bytes > bytes) return RTS_EWORKSPACE;
+    }
+    if (rows * plan.groups > kMaxGrid) return RTS_EUNSUPPORTED;
+    return rts::launch_topk_rows(logits, dtype, rows, cols, ld_logits, row_ends, k, out_idx, ld_out,
+                                 plan, scratch, stream);
+}
+
 int pack_candidates(const uint16_t* logits_bf16, int64_t rows, int64_t cols, int64_t ld_logits,
                     const int32_t* local_idx, int32_t n, int64_t ld_idx, const int32_t* row_ends,
                     int32_t* packed, hipStream_t stream) {

@@ -28,7 +28,15 @@ struct TopkPlan {
     size_t ws_bytes;
 };
 
+// Largest workspace a topk_rows plan uses: partial lists of split rows beyond
+// this take fewer groups.  Also the size of topk_rows_noalloc's static scratch.
+constexpr size_t kMaxSplitBytes = size_t(16) << 20;
+
 TopkPlan plan_topk_rows(int dtype, int64_t rows, int64_t cols, int32_t k, bool allow_split);
+
+// topk_rows_noalloc's scratch on the current device (its address there, taken
+// on the first call on the device) and its size in bytes.
+int scratch_of_current_device(void** ptr, size_t* bytes);
 
 int launch_topk_rows(const void* logits, int dtype, int64_t rows, int64_t cols, int64_t ld,
                      const int32_t* row_ends, int32_t k, int32_t* out, int64_t ld_out,

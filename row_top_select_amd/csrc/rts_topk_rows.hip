@@ -30,6 +30,8 @@
 //     second kernel merges them the same way.
 // The result is exact for any distribution; adversarial orders only cost more
 // compactions, never more HBM traffic.
+#include <mutex>
+
 #include "rts_device.hpp"
 #include "rts_internal.h"
 #include "../../include/row_top_select.h"
@@ -636,8 +638,43 @@ TopkPlan plan_topk_rows(int dtype, int64_t rows, int64_t cols, int32_t k, bool a
         if (gr > 256) gr = 256;
         if (gr >= 2) p.groups = (int)gr;
     }
+    // Partial lists stay within kMaxSplitBytes (fewer groups, or none).
+    const int64_t list_bytes = lp * (int64_t)sizeof(uint64_t);
+    while (p.groups > 1 && rows * p.groups * list_bytes > (int64_t)kMaxSplitBytes) --p.groups;
     if (p.groups > 1) p.ws_bytes = (size_t)rows * p.groups * lp * sizeof(uint64_t);
     return p;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of topk_rows_noalloc: the split rows' partial lists live in this
+// file-scope device array instead of a caller workspace.  Each device holds
+// its own copy at its own address, taken with hipGetSymbolAddress on the
+// first call on that device (with the device current) and kept; the array's
+// host-side name is never passed to a kernel.  Every list a launch reads was
+// written in full by the same launch, so nothing needs clearing; calls that
+// overlap on one device share the array and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint64_t scratch[kMaxSplitBytes / sizeof(uint64_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int scratch_of_current_device(void** ptr, size_t* bytes) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return RTS_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return RTS_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return RTS_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    *bytes = sizeof(scratch);
+    return RTS_OK;
 }
 
 int launch_topk_rows(const void* logits, int dtype, int64_t rows, int64_t cols, int64_t ld,

@@ -159,3 +159,30 @@ def test_second_round_layout_and_rows_validation(lib):
     kv.out_cols, kv.rows_out = 2048, None                                                # null rows_out
     assert lib.merge_rescue_rank_major_rows(FAKE, FAKE, 8, 4, 384, 2048, FAKE, ctypes.byref(kv),
                                             None, None) == EINVAL
+
+
+def test_topk_rows_noalloc_validation(lib):
+    EINVAL, EUNSUP = -1, -2
+    f = lib.topk_rows_noalloc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    assert f(FAKE, 2, 4, 8, 8, None, 2, FAKE, 2, None) == EINVAL        # dtype
+    assert f(FAKE, 0, 4, 8, 7, None, 2, FAKE, 2, None) == EINVAL        # ld < cols
+    assert f(FAKE, 0, 4, 8, 8, None, 0, FAKE, 2, None) == EINVAL        # k < 1
+    assert f(FAKE, 0, 4, 8, 8, None, 4, FAKE, 3, None) == EINVAL        # ld_out < k
+    assert f(FAKE, 0, 4, 8, 8, None, 2049, FAKE, 4096, None) == EUNSUP  # k > 2048
+    assert f(None, 0, 4, 8, 8, None, 2, FAKE, 2, None) == EINVAL        # null logits
+    assert f(ctypes.c_void_p(0x10001), 0, 4, 8, 8, None, 2, FAKE, 2, None) == EINVAL  # misaligned
+    assert f(FAKE, 0, 0, 8, 8, None, 2, FAKE, 2, None) == 0             # no rows: nothing to do
+
+
+def test_split_workspace_fits_the_static_scratch(lib):
+    # topk_rows_noalloc keeps split rows' partial lists in a 16 MiB static
+    # array: no launch plan may need more, for any shape.
+    worst = 0
+    for rows in list(range(1, 700)) + [1024, 4096, 1 << 20]:
+        for cols in (1000, 20000, 102400, 200000, 10 ** 6, 10 ** 7, (1 << 31) - 1):
+            for k in (1, 64, 65, 512, 513, 1024, 1025, 2048):
+                for dt in (0, 1):
+                    worst = max(worst, lib.topk_rows_workspace_size(dt, rows, cols, k))
+    assert 0 < worst <= 16 << 20
