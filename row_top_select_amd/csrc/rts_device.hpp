@@ -158,11 +158,12 @@ __device__ __forceinline__ uint64_t select64_by_mask(uint64_t m, uint64_t if_set
     return ((uint64_t)hi << 32) | lo;
 }
 
-template <int N, bool DESC, int K, int J>
-__device__ __forceinline__ void bitonic_stage(uint64_t (&v)[N]) {
+// flip = ~0: the whole network sorts descending (a wave-uniform value, so
+// the direction may also be chosen at run time).
+template <int N, int K, int J>
+__device__ __forceinline__ void bitonic_stage_flip(uint64_t (&v)[N], uint64_t flip) {
     // Element i = l*N + r lies in an ascending run iff (i & K) == 0 (the
-    // reverse for DESC).  For K >= N that is bit K/N of the lane.
-    constexpr uint64_t flip = DESC ? ~0ull : 0ull;
+    // reverse when flipped).  For K >= N that is bit K/N of the lane.
     if constexpr (J < N) {
 #pragma unroll
         for (int r = 0; r < N; ++r) {
@@ -178,9 +179,9 @@ __device__ __forceinline__ void bitonic_stage(uint64_t (&v)[N]) {
         }
     } else {
         constexpr int LJ = J / N;
-        constexpr uint64_t desc = lanes_with_bit(K / N) ^ flip;
+        const uint64_t desc = lanes_with_bit(K / N) ^ flip;
         // The lower partner keeps the smaller value in an ascending run.
-        constexpr uint64_t keep_max = lanes_with_bit(LJ) ^ desc;
+        const uint64_t keep_max = lanes_with_bit(LJ) ^ desc;
 #pragma unroll
         for (int r = 0; r < N; ++r) {
             const uint64_t o = shfl_xor64(v[r], LJ);
@@ -191,19 +192,19 @@ __device__ __forceinline__ void bitonic_stage(uint64_t (&v)[N]) {
 }
 
 // Stages J, J/2, .., 1 of the merge step of size K.
-template <int N, bool DESC, int K, int J>
-__device__ __forceinline__ void bitonic_steps(uint64_t (&v)[N]) {
+template <int N, int K, int J>
+__device__ __forceinline__ void bitonic_steps(uint64_t (&v)[N], uint64_t flip) {
     if constexpr (J >= 1) {
-        bitonic_stage<N, DESC, K, J>(v);
-        bitonic_steps<N, DESC, K, J / 2>(v);
+        bitonic_stage_flip<N, K, J>(v, flip);
+        bitonic_steps<N, K, J / 2>(v, flip);
     }
 }
 
-template <int N, bool DESC, int K>
-__device__ __forceinline__ void bitonic_sort_from(uint64_t (&v)[N]) {
+template <int N, int K>
+__device__ __forceinline__ void bitonic_sort_from(uint64_t (&v)[N], uint64_t flip) {
     if constexpr (K <= kWave * N) {
-        bitonic_steps<N, DESC, K, K / 2>(v);
-        bitonic_sort_from<N, DESC, K * 2>(v);
+        bitonic_steps<N, K, K / 2>(v, flip);
+        bitonic_sort_from<N, K * 2>(v, flip);
     }
 }
 
@@ -211,14 +212,29 @@ __device__ __forceinline__ void bitonic_sort_from(uint64_t (&v)[N]) {
 // instantiation, so k and j are constants without relying on loop unrolling.
 template <int N, bool DESC>
 __device__ __forceinline__ void wave_bitonic_sort(uint64_t (&v)[N]) {
-    bitonic_sort_from<N, DESC, 2>(v);
+    bitonic_sort_from<N, 2>(v, DESC ? ~0ull : 0ull);
 }
 
 // Sorts a bitonic sequence (e.g. the elementwise max of a descending and an
 // ascending sorted sequence).
 template <int N, bool DESC>
 __device__ __forceinline__ void wave_bitonic_merge(uint64_t (&v)[N]) {
-    bitonic_steps<N, DESC, kWave * N, kWave * N / 2>(v);
+    bitonic_steps<N, kWave * N, kWave * N / 2>(v, DESC ? ~0ull : 0ull);
+}
+
+// The same, with the direction a wave-uniform run-time value (read from the
+// first lane, so the masks derived from it stay scalar).
+__device__ __forceinline__ uint64_t uniform_flip(bool desc) {
+    const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane(desc ? -1 : 0);
+    return ((uint64_t)f << 32) | f;
+}
+template <int N>
+__device__ __forceinline__ void wave_bitonic_sort_dir(uint64_t (&v)[N], bool desc) {
+    bitonic_sort_from<N, 2>(v, uniform_flip(desc));
+}
+template <int N>
+__device__ __forceinline__ void wave_bitonic_merge_dir(uint64_t (&v)[N], bool desc) {
+    bitonic_steps<N, kWave * N, kWave * N / 2>(v, uniform_flip(desc));
 }
 
 // ---------------------------------------------------------------------------
@@ -284,13 +300,10 @@ __device__ __forceinline__ uint32_t wave_incl_scan32(uint32_t v) {
 // ---------------------------------------------------------------------------
 // Scans the bins from the top: finds the bin where the running count reaches
 // need, lowers need by the count above it and returns the bin and its count
-// (uniform).  False only if the counts were inconsistent.
-__device__ __forceinline__ bool radix_find(const uint32_t* hist, int& need, uint32_t& bin,
-                                           uint32_t& cb) {
-    const int lane = lane_id();
-    uint32_t c[4];  // lane l owns bins 255-4l .. 252-4l
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = hist[255 - 4 * lane - j];
+// (uniform).  False only if the counts were inconsistent.  c[j] is the count
+// of bin 255 - 4 * lane - j (lane l owns bins 255-4l .. 252-4l).
+__device__ __forceinline__ bool radix_find_counts(const uint32_t (&c)[4], int& need, uint32_t& bin,
+                                                  uint32_t& cb) {
     const uint32_t tot = c[0] + c[1] + c[2] + c[3];
     uint32_t run = wave_incl_scan32(tot) - tot;
     int fj = -1;
@@ -312,6 +325,54 @@ __device__ __forceinline__ bool radix_find(const uint32_t* hist, int& need, uint
     need -= (int)__builtin_amdgcn_readlane(above, fl);
     cb = __builtin_amdgcn_readlane(cl, fl);
     return true;
+}
+
+// radix_find over one 256-bin table.
+__device__ __forceinline__ bool radix_find(const uint32_t* hist, int& need, uint32_t& bin,
+                                           uint32_t& cb) {
+    const int lane = lane_id();
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = hist[255 - 4 * lane - j];
+    return radix_find_counts(c, need, bin, cb);
+}
+
+// ---------------------------------------------------------------------------
+// Wave-private 256-bin histogram in kStripes lane-striped copies: lane l
+// counts into copy l % kStripes, so lanes that share a bin mostly hit
+// different addresses.  Copies are kStripeStride words apart (16-byte
+// aligned, each copy's banks shifted by 4).
+// ---------------------------------------------------------------------------
+constexpr int kStripes = 4;
+constexpr int kStripeStride = 260;
+constexpr int kStripedWords = kStripes * kStripeStride;
+
+__device__ __forceinline__ void striped_clear(uint32_t* hist) {
+    const int lane = lane_id();  // lane l clears bins 16(l%16) .. +15 of copy l/16
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    u32x4_t* p = reinterpret_cast<u32x4_t*>(hist + (lane >> 4) * kStripeStride + 16 * (lane & 15));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
+__device__ __forceinline__ void striped_add(uint32_t* hist, uint32_t bin) {
+    __hip_atomic_fetch_add(&hist[(lane_id() & (kStripes - 1)) * kStripeStride + bin], 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
+// radix_find over the sum of the striped copies.
+__device__ __forceinline__ bool striped_find(const uint32_t* hist, int& need, uint32_t& bin,
+                                             uint32_t& cb) {
+    const int lane = lane_id();
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    // bins 252-4l .. 255-4l: one 16-byte read per copy, the copies summed
+    // one after the other (a real loop: the caller holds many registers)
+    u32x4_t acc = *reinterpret_cast<const u32x4_t*>(hist + 252 - 4 * lane);
+#pragma unroll 1
+    for (int s = 1; s < kStripes; ++s)
+        acc += *reinterpret_cast<const u32x4_t*>(hist + s * kStripeStride + 252 - 4 * lane);
+    const uint32_t c[4] = {acc[3], acc[2], acc[1], acc[0]};
+    return radix_find_counts(c, need, bin, cb);
 }
 
 }  // namespace rts

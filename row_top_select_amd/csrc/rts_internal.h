@@ -26,6 +26,7 @@ struct TopkPlan {
     int waves;      // waves per workgroup sharing one row
     int groups;     // workgroups per row (> 1 needs a workspace)
     size_t ws_bytes;
+    int block_kpt;  // > 0: whole rows in one workgroup's registers, block_kpt keys per thread
 };
 
 // Largest workspace a topk_rows plan uses: partial lists of split rows beyond

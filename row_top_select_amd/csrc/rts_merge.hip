@@ -682,12 +682,17 @@ __global__ __launch_bounds__(256) void emit_rows_kernel(
 // the output position.
 //   1. ord16 threshold: 256-bin levels over the score half of the words in
 //      [min, max] of the nonzero ones (one level when the scores span fewer
-//      than 256 ord16 values, two at most).
+//      than 256 ord16 values, two at most).  The bins are counted in four
+//      lane-striped copies: bf16 scores crowd into a few bins of the first
+//      level (a bin is a binade there), and lanes sharing a bin then mostly
+//      hit different addresses.
 //   2. Ties at tau16 (the k-th score): the candidates tied there are taken by
 //      ascending gid; up to 64 of them are sorted in one register, more go
 //      through 256-bin levels over the gid.
 //   3. Emission in candidate order, -1 tail; tau16 and the saturation mask
-//      come out of the same pass.
+//      come out of the same pass.  A score test on the whole word: ord16 >
+//      thr  <=>  word > (thr << 16 | 0xFFFF), and "empty or ord16 <= tau16"
+//      <=>  word < (tau16 + 1) << 16.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t packed_gid(uint32_t word, uint32_t hibit, uint32_t world, uint32_t r) {
     const uint32_t local = (0xFFFFu - (word & 0xFFFFu)) | (hibit << 16);
@@ -701,7 +706,7 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
     constexpr int NR = QN * W;  // registers: rank r = i / QN, q = i % QN
     constexpr int32_t world = W;
     (void)world_;
-    __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kStripedWords];
     __shared__ uint32_t tied[kWave];
     const int lane = lane_id();
     const int64_t row = blockIdx.x;
@@ -768,18 +773,16 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
     for (int level = 0; level < 2; ++level) {  // a 16-bit score needs two levels at most
         fresh();
         if (open) {
-            *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+            striped_clear(hist);
             wave_lds_sync();
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
                 const uint32_t x = (w[i] >> 16) - wlo;  // empty: wraps past span
-                if (x <= span)
-                    __hip_atomic_fetch_add(&hist[x >> sh], 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_WAVEFRONT);
+                if (x <= span) striped_add(hist, x >> sh);
             }
             wave_lds_sync();
             uint32_t bin, cb;
-            if (!radix_find(hist, need, bin, cb)) {  // only if counts were inconsistent
+            if (!striped_find(hist, need, bin, cb)) {  // only if counts were inconsistent
                 thr_gt = wlo - 1u;
                 tau_from_min = true;
                 open = false;
@@ -810,7 +813,8 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
         thr_gt = wlo - 1u;
         tau_from_min = true;
     }
-    // Up to 64 tied candidates: sort their gids in one register.
+    // Up to 64 tied candidates: sort their gids in one register.  A register
+    // with no tied lane (most of them) costs a compare and a ballot.
     fresh();
     if (ties && ntied <= (uint32_t)kWave) {
         int base = 0;
@@ -818,8 +822,11 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
         for (int i = 0; i < NR; ++i) {
             const bool t = (w[i] >> 16) == tie16;
             const uint64_t m = __ballot(t);
-            if (t) tied[base + (int)mbcnt64(m)] = packed_gid(w[i], hibit(i), (uint32_t)world, (uint32_t)(i / QN));
-            base += (int)__popcll(m);
+            if (m) {
+                if (t) tied[base + (int)mbcnt64(m)] =
+                    packed_gid(w[i], hibit(i), (uint32_t)world, (uint32_t)(i / QN));
+                base += (int)__popcll(m);
+            }
         }
         wave_lds_sync();
         uint64_t sv[1] = {lane < (int)ntied ? (uint64_t)tied[lane] : ~0ull};
@@ -834,7 +841,7 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
         for (int gl = 0; gl < 3; ++gl) {
             fresh();
             if (gopen) {
-                *reinterpret_cast<uint4*>(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+                striped_clear(hist);
                 wave_lds_sync();
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
@@ -842,14 +849,12 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
                         const uint32_t key = ((1u << 21) - 1u) -
                             packed_gid(w[i], hibit(i), (uint32_t)world, (uint32_t)(i / QN));
                         const uint32_t x = key - gw;
-                        if (x <= gspan)
-                            __hip_atomic_fetch_add(&hist[x >> gs], 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_WAVEFRONT);
+                        if (x <= gspan) striped_add(hist, x >> gs);
                     }
                 }
                 wave_lds_sync();
                 uint32_t gbin, gcb;
-                if (!radix_find(hist, need, gbin, gcb)) {
+                if (!striped_find(hist, need, gbin, gcb)) {
                     gopen = false;
                 } else {
                     gw += gbin << gs;
@@ -878,13 +883,20 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
 
     // Emission in candidate order; saturation: rank r keeps its bit iff all n
     // of its words are nonzero with a score above tau16.  Owned physical rows
-    // (when requested) are the selected words of rank dcp_rank, in the same order.
+    // (when requested) are the selected words of rank dcp_rank, in the same
+    // order.  thr_gt <= 0xFF80 (the largest ord16) and tau16 <= 0xFF80, so
+    // neither word bound overflows.
     int32_t* o_row = out_ids ? out_ids + row * (int64_t)k : nullptr;
     constexpr bool want_rows = ROWS;
     const int32_t* bt = want_rows ? rows_table_of(ra, row) : nullptr;
     int32_t* r_row = want_rows ? ra.rows_out + row * (int64_t)ra.out_cols : nullptr;
+    const uint32_t sel_w = (thr_gt << 16) | 0xFFFFu;  // word > sel_w  <=>  ord16 > thr_gt
+    const uint32_t sat_w = (tau16 + 1u) << 16;        // word < sat_w  <=>  empty or ord16 <= tau16
     int base = 0, rbase = 0;
     uint32_t notsat = 0u;
+    // One emission loop for both cases (without ties, tie16 = 0 matches no
+    // nonzero word): two specialised loops would let the compiler hoist the
+    // gids of every register above the branch.
     fresh();
 #pragma unroll
     for (int r = 0; r < W; ++r) {
@@ -892,14 +904,13 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
 #pragma unroll
         for (int q = 0; q < QN; ++q) {
             const int i = r * QN + q;
-            const uint32_t o = w[i] >> 16;
             const uint32_t gid = packed_gid(w[i], hibit(i), (uint32_t)world, (uint32_t)r);
-            const bool sel = w[i] != 0u && (o > thr_gt || (o == tie16 && gid <= gid_cut));
+            const bool sel = w[i] > sel_w || ((w[i] >> 16) == tie16 && gid <= gid_cut);
             const uint64_t m = __ballot(sel);
             const int pos = base + (int)mbcnt64(m);
             if (o_row && sel && pos < k) o_row[pos] = (int32_t)gid;
             base += (int)__popcll(m);
-            bad |= __ballot((q < QN - 1 || q * kWave + lane < n) && (w[i] == 0u || o <= tau16));
+            bad |= __ballot((q < QN - 1 || q * kWave + lane < n) && w[i] < sat_w);
             if (want_rows && r == ra.dcp_rank) {  // uniform
                 int32_t phys = -1;
                 const bool own = sel && owned_phys(ra, bt, gid / (uint32_t)world, phys);

@@ -34,6 +34,7 @@
 
 #include "rts_device.hpp"
 #include "rts_internal.h"
+#include "rts_levels.hpp"
 #include "../../include/row_top_select.h"
 
 namespace rts {
@@ -442,8 +443,25 @@ void topk_rows_stream_kernel(
         }
         // Every entry has key >= thr_own - 1: the list's entries are at or
         // above its k-th key, and the filter passes keys >= thr_own (-0 also
-        // passes a +0 threshold, one key below).
-        const uint64_t T0 = nl + cnt > k ? wave_kth<E + ES>(v, k, thr_own - 1u, hist) : 1ull;
+        // passes a +0 threshold, one key below).  Until the list first holds
+        // k entries that bound is the key of -inf, far below the entries:
+        // the window then starts at their smallest key, or concentrated
+        // scores (all inside one binade) would share a few bins of the first
+        // levels and serialise their histogram atomics.
+        uint64_t T0 = 1ull;
+        if (nl + cnt > k) {
+            uint32_t lb = thr_own - 1u;
+            if (nl < k) {
+                uint32_t m1 = 0xFFFFFFFFu;  // min of key - 1: empty slots (key 0) wrap to the top
+#pragma unroll
+                for (int r = 0; r < E + ES; ++r) {
+                    const uint32_t km1 = (uint32_t)(v[r] >> 32) - 1u;
+                    m1 = km1 < m1 ? km1 : m1;
+                }
+                lb = wave_min32(m1) + 1u;
+            }
+            T0 = wave_kth<E + ES>(v, k, lb, hist);
+        }
         int base = 0;
         uint32_t kmin = 0xFFFFFFFFu;
 #pragma unroll
@@ -509,18 +527,278 @@ void topk_rows_stream_kernel(
     }
 
     if (wave == 0) {
+        // An opaque copy of the lane index: without it the compiler computes
+        // the output positions at the start and holds them through the stream.
+        int lane_o = lane;
+        asm volatile("" : "+v"(lane_o));
         if (groups == 1) {
             int32_t* o = out + row * ld_out;
 #pragma unroll
             for (int r = 0; r < E; ++r) {
-                const int i = lane * E + r;
+                const int i = lane_o * E + r;
                 if (i < k) o[i] = L[r] ? (int32_t)composite_id(L[r]) : -1;
             }
         } else {
             uint64_t* p = part + ((int64_t)row * groups + g) * LP;
 #pragma unroll
-            for (int r = 0; r < E; ++r) p[lane * E + r] = L[r];
+            for (int r = 0; r < E; ++r) p[lane_o * E + r] = L[r];
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Short rows with a large k: one workgroup of NW waves holds the whole row in
+// registers (KPT keys per thread, the column implied by the position), so a
+// row costs one read and no compaction however many candidates survive.
+//   1. key32 of every element (0 for NaN and columns at or past the row end);
+//      valid count and [min, max] of the valid keys;
+//   2. workgroup radix levels over the keys (256 bins of the live window,
+//      lane-striped LDS histogram copies), then the tie rule at the k-th key
+//      by ascending column;
+//   3. the selected (exactly min(k, valid)) are written to LDS as composites
+//      and sorted descending by a bitonic network over the workgroup: each
+//      wave sorts 64*E in registers (even waves descending, odd ascending),
+//      then the cross-wave steps exchange through LDS and each wave finishes
+//      with an in-register merge.
+// Element i of thread t's keys: columns 4 * (g * 64 * NW + t) + j for
+// i = 4g + j, so each group of four is one 16-byte (fp32) or 8-byte (bf16)
+// load and a wave's load covers 1 KB (512 B) of the row.
+// ---------------------------------------------------------------------------
+template <int NW>
+struct BlockRowSmem {
+    uint32_t hist[kLevelCopies][kLevelStride];
+    uint32_t bins[256];
+    uint32_t bc[4];
+    uint32_t tied[kWave];
+    uint32_t ntied;
+    uint32_t red[NW][4];
+};
+
+template <int NW, int KPT, int E, bool BF16>
+__global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
+    const void* __restrict__ xv, int64_t cols, int64_t ld, const int32_t* __restrict__ row_ends,
+    int32_t k, int32_t* __restrict__ out, int64_t ld_out) {
+    using T = typename RowTraits<BF16>::elem;
+    using V = typename RowTraits<BF16>::vec;
+    constexpr int NT = kWave * NW;
+    constexpr int S = kWave * E;  // sort slots per wave
+    constexpr int LS = S * NW;    // sort slots of the workgroup (>= k)
+    static_assert(KPT % 4 == 0, "keys come in groups of four");
+    __shared__ BlockRowSmem<NW> sm;
+    __shared__ uint64_t buf[LS];
+    const int t = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int64_t row = blockIdx.x;
+    int64_t e = row_ends ? (int64_t)row_ends[row] : cols;
+    e = e < 0 ? 0 : (e > cols ? cols : e);
+    const T* rowp = reinterpret_cast<const T*>(xv) + row * ld;
+
+    for (int q = t; q < kLevelCopies * kLevelStride; q += NT) (&sm.hist[0][0])[q] = 0u;
+    if (t == 0) sm.ntied = 0u;
+
+    // Column of key i, from the thread's base column 4t.  Each pass takes an
+    // opaque copy of the base, so the compiler cannot keep KPT column values
+    // live from pass to pass.
+    auto col_base = [&]() -> uint32_t {
+        uint32_t b = 4u * (uint32_t)t;
+        asm volatile("" : "+v"(b));
+        return b;
+    };
+    auto col_at = [](uint32_t base, int i) -> uint32_t {
+        return base + (uint32_t)(4 * (i >> 2) * NT + (i & 3));
+    };
+    // Every whole group of four inside the row end is one vector load, all
+    // issued before any is used; a group cut by the row end, or every group
+    // of a row not aligned to a vector, is read element by element.
+    const bool vec_ok = (reinterpret_cast<uintptr_t>(rowp) % sizeof(V)) == 0;
+    uint32_t key[KPT];
+    {
+        V raw[KPT / 4];
+        const int64_t t4 = 4 * (int64_t)t;
+#pragma unroll
+        for (int g = 0; g < KPT / 4; ++g) {
+            const int64_t c0 = (int64_t)g * NT * 4 + t4;
+            raw[g] = V{};
+            if (vec_ok && c0 + 4 <= e) raw[g] = __builtin_nontemporal_load(reinterpret_cast<const V*>(rowp + c0));
+        }
+#pragma unroll
+        for (int g = 0; g < KPT / 4; ++g) {
+            const int64_t c0 = (int64_t)g * NT * 4 + t4;
+            uint32_t bits[4];
+            unpack<BF16>(raw[g], bits);
+            if (c0 < e && (!vec_ok || c0 + 4 > e)) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bits[j] = c0 + j < e ? load_bits<BF16>(rowp + c0 + j) : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool ok = c0 + j < e && !f32_bits_is_nan(bits[j]);
+                key[4 * g + j] = ok ? key32_of_bits(bits[j]) : 0u;
+            }
+        }
+    }
+
+    // Valid count and key range (every valid key is >= key32(-inf) > 0; the
+    // minimum is taken over key - 1, which sends empty slots to the top).
+    uint32_t nv = 0, mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        nv += (uint32_t)__popcll(__ballot(key[i] != 0u));
+        const uint32_t km1 = key[i] - 1u;
+        mn = km1 < mn ? km1 : mn;
+        mx = key[i] > mx ? key[i] : mx;
+    }
+    mn = wave_min32(mn);
+    mx = wave_max32(mx);
+    if (lane == 0) {
+        sm.red[wave][0] = nv;
+        sm.red[wave][1] = mn;
+        sm.red[wave][2] = mx;
+    }
+    lds_barrier();
+    nv = 0;
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        nv += sm.red[w][0];
+        mn = sm.red[w][1] < mn ? sm.red[w][1] : mn;
+        mx = sm.red[w][2] > mx ? sm.red[w][2] : mx;
+    }
+    mn += 1u;
+
+    // Selected: key > thr_gt, or key == tie_key and column <= col_cut.
+    uint32_t thr_gt = 0u, tie_key = 0u, col_cut = 0u;
+    if (nv > (uint32_t)k) {
+        auto visit = [&](auto f) __attribute__((always_inline)) {
+            const uint32_t cb = col_base();
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) f(key[i], col_at(cb, i));
+        };
+        int need = k;
+        uint32_t wlo = mn, whi = mx;
+        bool done = false;
+        // First level in score space: bins of the score range, linear in
+        // the value.  bin(v) = min(255, (v - lo) * 256 / (hi - lo)) is
+        // monotone in the key (rounding is monotone; +-0 share a bin), so the
+        // keys of a bin form one key range.  Key-space bins of the full range
+        // are a binade wide and would put a bell-shaped row into a handful of
+        // bins.  Infinite or degenerate ranges skip this level.
+        const float lo = float_of_key32(mn), hi = float_of_key32(mx);
+        const float scale = 256.0f / (hi - lo);
+        if (__builtin_isfinite(lo) && __builtin_isfinite(hi) && hi > lo && __builtin_isfinite(scale)) {
+            auto vbin = [&](uint32_t kk) -> uint32_t {
+                const float tb = (float_of_key32(kk) - lo) * scale;  // in [0, 256]
+                return (uint32_t)(tb < 255.0f ? tb : 255.0f);
+            };
+#pragma unroll
+            for (int i = 0; i < KPT; ++i)
+                if (key[i] != 0u)
+                    __hip_atomic_fetch_add(&sm.hist[lane & (kLevelCopies - 1)][vbin(key[i])], 1u,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            uint32_t bin, cbin;
+            if (level_hist_find(sm, need, bin, cbin)) {
+                // Key range of the boundary bin.
+                uint32_t bmn = 0xFFFFFFFFu, bmx = 0u;
+#pragma unroll
+                for (int i = 0; i < KPT; ++i) {
+                    const bool in = key[i] != 0u && vbin(key[i]) == bin;
+                    bmn = in && key[i] < bmn ? key[i] : bmn;
+                    bmx = in && key[i] > bmx ? key[i] : bmx;
+                }
+                bmn = wave_min32(bmn);
+                bmx = wave_max32(bmx);
+                if (lane == 0) {
+                    sm.red[wave][1] = bmn;
+                    sm.red[wave][2] = bmx;
+                }
+                lds_barrier();
+                bmn = 0xFFFFFFFFu;
+                bmx = 0u;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    bmn = sm.red[w][1] < bmn ? sm.red[w][1] : bmn;
+                    bmx = sm.red[w][2] > bmx ? sm.red[w][2] : bmx;
+                }
+                lds_barrier();
+                if ((int)cbin == need) {  // the whole bin is taken: keys >= its smallest
+                    thr_gt = bmn - 1u;
+                    done = true;
+                } else {
+                    wlo = bmn;
+                    whi = bmx;
+                }
+            }
+        }
+        if (!done) {
+            const uint32_t span = whi - wlo;
+            const int bl = span ? 32 - __clz((int)span) : 0;
+            const uint32_t sh = bl > 8 ? (uint32_t)(bl - 8) : 0u;
+            bool ties;
+            uint32_t ntie;
+            radix_levels(sm, visit, need, wlo, span, sh, whi, thr_gt, ties, tie_key, ntie);
+            if (ties) col_cut = tie_cut(sm, visit, tie_key, ntie, need);
+        }
+    }
+    auto selected = [&](uint32_t kk, uint32_t c) {
+        return kk != 0u && (kk > thr_gt || (kk == tie_key && c <= col_cut));
+    };
+
+    // The selected composites into LDS (any order), empty slots after them.
+    uint32_t cnt = 0;
+    uint32_t cb = col_base();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) cnt += (uint32_t)__popcll(__ballot(selected(key[i], col_at(cb, i))));
+    if (lane == 0) sm.red[wave][3] = cnt;
+    lds_barrier();
+    uint32_t off = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        off += w < wave ? sm.red[w][3] : 0u;
+        total += sm.red[w][3];
+    }
+    cb = col_base();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const uint32_t c = col_at(cb, i);
+        const bool sel = selected(key[i], c);
+        const uint64_t m = __ballot(sel);
+        const uint32_t pos = off + mbcnt64(m);
+        if (sel && pos < (uint32_t)LS) buf[pos] = composite(key[i], c);
+        off += (uint32_t)__popcll(m);
+    }
+    for (int p = (int)(total < (uint32_t)LS ? total : (uint32_t)LS) + t; p < LS; p += NT) buf[p] = 0ull;
+    lds_barrier();
+
+    // Descending sort of the LS slots; element i = wave * S + lane * E + r.
+    uint64_t v[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) v[r] = buf[wave * S + lane * E + r];
+    wave_bitonic_sort_dir<E>(v, (wave & 1) == 0);
+#pragma unroll
+    for (int K = 2 * S; K <= LS; K *= 2) {
+        const bool desc = ((wave * S) & K) == 0;
+#pragma unroll
+        for (int J = K / 2; J >= S; J /= 2) {
+            lds_barrier();
+#pragma unroll
+            for (int r = 0; r < E; ++r) buf[wave * S + lane * E + r] = v[r];
+            lds_barrier();
+            const int pw = wave ^ (J / S);
+            const bool keep_max = (wave < pw) == desc;
+#pragma unroll
+            for (int r = 0; r < E; ++r) {
+                const uint64_t o = buf[pw * S + lane * E + r];
+                v[r] = keep_max ? umax64(v[r], o) : umin64(v[r], o);
+            }
+        }
+        wave_bitonic_merge_dir<E>(v, desc);
+    }
+    int32_t* o_row = out + row * ld_out;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int i = wave * S + lane * E + r;
+        if (i < k) o_row[i] = v[r] ? (int32_t)composite_id(v[r]) : -1;
     }
 }
 
@@ -619,9 +897,24 @@ void launch_e(bool bf16, int p, const void* x, int64_t rows, int64_t cols, int64
 
 }  // namespace
 
+// Whole rows in one workgroup (topk_rows_block_kernel): 32 keys per thread,
+// 4 waves for rows of up to 8192 columns, 8 up to 16384.
+constexpr int kBlockKeys = 32;
+constexpr int64_t kBlockMaxCols = (int64_t)kWave * 8 * kBlockKeys;
+
 TopkPlan plan_topk_rows(int dtype, int64_t rows, int64_t cols, int32_t k, bool allow_split) {
     (void)dtype;
-    TopkPlan p{list_e(k), 1, 1, 0};
+    TopkPlan p{list_e(k), 1, 1, 0, 0};
+    // Short rows and k > 1024: the streaming kernel's list of 2048 per wave
+    // holds 64 registers per lane (two waves per SIMD) and compacts after
+    // every 512 survivors; a whole row in a workgroup's registers is read
+    // once and selected without compactions (measured on 6710 x 16384 rows:
+    // faster for k = 2048, slower for k <= 1024).  Enough rows to fill the GPU.
+    if (k > 1024 && cols <= kBlockMaxCols && rows >= 256) {
+        p.block_kpt = kBlockKeys;
+        p.waves = cols <= kBlockMaxCols / 2 ? 4 : 8;
+        return p;
+    }
     const int64_t lp = (int64_t)kWave * p.e;
     const int64_t want = rows > 0 ? (kTargetWaves + rows - 1) / rows : 1;
     // Pieces long enough that compactions stay a small part of the work: the
@@ -677,11 +970,50 @@ int scratch_of_current_device(void** ptr, size_t* bytes) {
     return RTS_OK;
 }
 
+namespace {
+
+template <int NW, int E, bool BF16>
+void launch_block(const void* x, int64_t rows, int64_t cols, int64_t ld, const int32_t* re, int32_t k,
+                  int32_t* out, int64_t ld_out, hipStream_t s) {
+    hipLaunchKernelGGL((topk_rows_block_kernel<NW, kBlockKeys, E, BF16>), dim3((unsigned)rows),
+                       dim3(kWave * NW), 0, s, x, cols, ld, re, k, out, ld_out);
+}
+
+// E: sort slots per lane, 64 * NW * E >= k.
+template <int NW, bool BF16>
+int launch_block_e(const void* x, int64_t rows, int64_t cols, int64_t ld, const int32_t* re, int32_t k,
+                   int32_t* out, int64_t ld_out, hipStream_t s) {
+    constexpr int S1 = kWave * NW;  // k in (1024, 2048]
+    if (k <= 4 * S1 && NW == 8) launch_block<NW, 4, BF16>(x, rows, cols, ld, re, k, out, ld_out, s);
+    else if (k <= 8 * S1) launch_block<NW, 8, BF16>(x, rows, cols, ld, re, k, out, ld_out, s);
+    else return RTS_EUNSUPPORTED;
+    return RTS_OK;
+}
+
+int launch_block_rows(bool bf16, int waves, const void* x, int64_t rows, int64_t cols, int64_t ld,
+                      const int32_t* re, int32_t k, int32_t* out, int64_t ld_out, hipStream_t s) {
+    if (waves == 4)
+        return bf16 ? launch_block_e<4, true>(x, rows, cols, ld, re, k, out, ld_out, s)
+                    : launch_block_e<4, false>(x, rows, cols, ld, re, k, out, ld_out, s);
+    if (waves == 8)
+        return bf16 ? launch_block_e<8, true>(x, rows, cols, ld, re, k, out, ld_out, s)
+                    : launch_block_e<8, false>(x, rows, cols, ld, re, k, out, ld_out, s);
+    return RTS_EUNSUPPORTED;
+}
+
+}  // namespace
+
 int launch_topk_rows(const void* logits, int dtype, int64_t rows, int64_t cols, int64_t ld,
                      const int32_t* row_ends, int32_t k, int32_t* out, int64_t ld_out,
                      const TopkPlan& plan, void* workspace, hipStream_t s) {
     if (rows == 0) return RTS_OK;
     const bool bf16 = dtype == RTS_BF16;
+    if (plan.block_kpt > 0) {
+        const int rc = launch_block_rows(bf16, plan.waves, logits, rows, cols, ld, row_ends, k, out,
+                                         ld_out, s);
+        if (rc != RTS_OK) return rc;
+        return hipGetLastError() == hipSuccess ? RTS_OK : RTS_EHIP;
+    }
     uint64_t* part = reinterpret_cast<uint64_t*>(workspace);
     const int p = plan.waves, g = plan.groups;
     switch (plan.e) {

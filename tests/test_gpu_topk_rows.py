@@ -239,3 +239,68 @@ def test_verylong_bf16_every_row(rts):
     got = host(rts.topk_rows(bf16_dev(xb), w.k, row_ends=dev(ends)))
     say("verylong bf16 oracle")
     assert_ids_equal(got, oracle.topk_rows(xb, ends, w.k), "verylong bf16")
+
+
+# Short rows with a large k (k > 1024, rows of at most 16384 columns, 256 rows
+# or more) take the whole-row-in-registers kernel; the rest of this file's
+# shapes stream (1024 and 777 below stream, as neighbours).  Every row against
+# the oracle.
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("cols,k", [(16384, 2048), (16384, 1024), (8192, 2048), (8192, 1025),
+                                    (3001, 1500), (12289, 777), (700, 2048), (16000, 1100)])
+def test_block_rows_random(rts, dtype, cols, k):
+    rng = np.random.default_rng(cols + k + (dtype == "bf16"))
+    rows = 300
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    ends = rng.integers(-3, cols + 20, size=rows).astype(np.int32)
+    ends[:4] = [cols, 0, min(k - 1, cols), min(k + 1, cols)]
+    say("block rows", dtype, cols, k)
+    if dtype == "bf16":
+        check(rts, datagen.bf16_bits(x), ends, k, "bf16", what=f"block bf16 {cols} {k}")
+    else:
+        check(rts, x, ends, k, what=f"block {cols} {k}")
+
+
+@pytest.mark.parametrize("case", ["ties", "specials", "equal", "ascending", "plus100"])
+def test_block_rows_adversarial(rts, case):
+    rng = np.random.default_rng(17)
+    rows, cols, k = 260, 16384, 2048
+    if case == "ties":
+        x = rng.integers(0, 64, size=(rows, cols)).astype(np.float32)
+    elif case == "specials":
+        x = rng.standard_normal((rows, cols)).astype(np.float32)
+        u = rng.random((rows, cols))
+        x[u < 0.01] = np.inf
+        x[(u >= 0.01) & (u < 0.02)] = -np.inf
+        x[(u >= 0.02) & (u < 0.05)] = np.nan
+        x[(u >= 0.05) & (u < 0.06)] = -0.0
+        x[(u >= 0.06) & (u < 0.07)] = 0.0
+        x[:8] = np.nan                       # rows with no candidate at all
+        x[8:16, ::3] = np.nan
+    elif case == "equal":
+        x = np.full((rows, cols), 1.25, np.float32)
+    elif case == "ascending":
+        x = np.tile(np.arange(cols, dtype=np.float32), (rows, 1))
+    else:
+        x = rng.standard_normal((rows, cols)).astype(np.float32) + np.float32(100.0)
+    ends = np.full(rows, cols, np.int32)
+    ends[1::7] = rng.integers(0, cols, size=len(ends[1::7]))
+    say("block adversarial", case)
+    check(rts, x, ends, k, what=f"block {case}")
+
+
+def test_block_rows_strided_and_misaligned(rts):
+    # logits starting one element past a 16-byte boundary (element loads) and
+    # an output wider than k (columns past k untouched)
+    rng = np.random.default_rng(23)
+    rows, cols, k = 270, 9000, 1100
+    big = rng.standard_normal((rows, cols + 1)).astype(np.float32)
+    xt = dev(big)[:, 1:]
+    out = torch.full((rows, k + 5), 777, dtype=torch.int32, device="cuda")
+    ends = rng.integers(0, cols + 1, size=rows).astype(np.int32)
+    say("block misaligned")
+    rts.topk_rows(xt, k, row_ends=dev(ends), out=out)
+    got = host(out)
+    assert (got[:, k:] == 777).all()
+    assert_ids_equal(got[:, :k], oracle.topk_rows(np.ascontiguousarray(big[:, 1:]), ends, k),
+                     "block misaligned")
