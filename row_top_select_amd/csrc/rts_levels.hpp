@@ -117,11 +117,12 @@ __device__ __forceinline__ void radix_levels(Smem& sm, Visit visit, int& need, u
 }
 
 // The largest id taken among the ntie entries with key == tie_key, when the
-// `need` lowest ids are taken (ids below 2^31): a wave sort for up to 64, else levels over
-// 2^31 - 1 - id.
+// `need` lowest ids are taken (ids at most id_hi < 2^31): a wave sort for up
+// to 64, else levels over id_hi - id.
 template <typename Smem, typename Visit>
 __device__ __forceinline__ uint32_t tie_cut(Smem& sm, Visit visit, uint32_t tie_key,
-                                                 uint32_t ntie, int need) {
+                                                 uint32_t ntie, int need,
+                                                 uint32_t id_hi = 0x7FFFFFFFu) {
     const int lane = lane_id();
     if (ntie <= (uint32_t)kWave) {
         visit([&](uint32_t key, uint32_t id) __attribute__((always_inline)) {
@@ -146,20 +147,23 @@ __device__ __forceinline__ uint32_t tie_cut(Smem& sm, Visit visit, uint32_t tie_
         lds_barrier();
         return cut;
     }
-    uint32_t gw = 0u, gspan = 0x7FFFFFFFu, gs = 23u;
+    uint32_t gw = 0u, gspan = id_hi;
+    const int gbl = gspan ? 32 - __clz((int)gspan) : 0;
+    uint32_t gs = gbl > 8 ? (uint32_t)(gbl - 8) : 0u;
 #pragma unroll 1
     for (int gl = 0; gl < 4; ++gl) {
         visit([&](uint32_t key, uint32_t id) __attribute__((always_inline)) {
-            if (key == tie_key) level_hist_add(sm, 0x7FFFFFFFu - id, gw, gspan, gs);
+            if (key == tie_key) level_hist_add(sm, id_hi - id, gw, gspan, gs);
         });
         uint32_t gbin, gcb;
         if (!level_hist_find(sm, need, gbin, gcb)) break;
         gw += gbin << gs;
         if ((int)gcb == need || gs == 0) break;
-        gspan = (1u << gs) - 1u;
+        const uint32_t top = id_hi - gw, width = (1u << gs) - 1u;
+        gspan = width < top ? width : top;
         gs = gs > 8 ? gs - 8 : 0u;
     }
-    return 0x7FFFFFFFu - gw;
+    return id_hi - gw;
 }
 
 }  // namespace rts

@@ -118,17 +118,20 @@ __device__ __forceinline__ void radix_hist(const uint64_t (&v)[NV], uint32_t w, 
 }
 
 // T such that exactly `need` nonzero entries of v[] are >= T (composites are
-// distinct).  Requires at least `need` nonzero entries, all with key >= lb.
+// distinct).  Requires at least `need` nonzero entries, all with key >= lb
+// and low word in [id_lo, id_lo + id_span] (the piece's columns).
 template <int NV>
 __device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[NV], int need, uint32_t lb,
-                                             uint32_t* hist) {
+                                             uint32_t id_lo, uint32_t id_span, uint32_t* hist) {
     uint32_t mx = 0;
 #pragma unroll
     for (int r = 0; r < NV; ++r) mx = mx > (uint32_t)(v[r] >> 32) ? mx : (uint32_t)(v[r] >> 32);
     mx = wave_max32(mx);
     // Key levels: s starts at most at 24 and drops by 8, so the fourth level
     // has s == 0 (bins of one key).
-    uint32_t w = lb, span = mx - lb;
+    // The window is [w, whi] (whi = w + span); every entry above it has
+    // already been counted out of `need`.
+    uint32_t w = lb, whi = mx, span = mx - lb;
     const int bl = span ? 32 - __clz((int)span) : 0;
     uint32_t s = bl > 8 ? (uint32_t)(bl - 8) : 0u;
 #pragma unroll 1
@@ -140,14 +143,42 @@ __device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[NV], int need, 
         if ((int)cb == need) return (uint64_t)blo << 32;
         w = blo;
         if (s == 0) break;  // the k-th key is tied
-        // Entries never exceed mx, so the window stays below 2^32.
-        const uint32_t top = mx - blo, width = (1u << s) - 1u;
+        // The chosen bin, clipped to the window (entries never exceed mx, so
+        // the window stays below 2^32).
+        const uint32_t top = whi - blo, width = (1u << s) - 1u;
         span = width < top ? width : top;
-        s = s > 8 ? s - 8 : 0u;
+        whi = w + span;
+        if (cb > (uint32_t)kWave) {
+            // A crowded bin: narrow the window to the keys actually in it.
+            // All equal (ties at the k-th key): straight to the tie levels,
+            // instead of levels that would count every entry into one bin.
+            uint32_t bmn = 0xFFFFFFFFu, bmx = 0u;
+#pragma unroll
+            for (int r = 0; r < NV; ++r) {
+                const uint32_t kr = (uint32_t)(v[r] >> 32);
+                const bool in = kr - w <= span;
+                bmn = in && kr < bmn ? kr : bmn;
+                bmx = in && kr > bmx ? kr : bmx;
+            }
+            bmn = wave_min32(bmn);
+            bmx = wave_max32(bmx);
+            w = bmn;
+            if (bmn == bmx) break;
+            whi = bmx;
+            span = bmx - bmn;
+            const int b2 = 32 - __clz((int)span);
+            s = b2 > 8 ? (uint32_t)(b2 - 8) : 0u;
+        } else {
+            s = s > 8 ? s - 8 : 0u;
+        }
     }
-    // Tie levels on the low word among the entries with key w.
+    // Tie levels on the low word among the entries with key w, over the
+    // piece's columns only (the full 32-bit window would spend its first
+    // levels with every tied entry in one bin).
     const uint32_t key = w;
-    uint32_t wl = 0, spl = 0xFFFFFFFFu, sl = 24;
+    uint32_t wl = id_lo, spl = id_span;
+    const int bll = spl ? 32 - __clz((int)spl) : 0;
+    uint32_t sl = bll > 8 ? (uint32_t)(bll - 8) : 0u;
 #pragma unroll 1
     for (int level = 0; level < 4; ++level) {
         radix_hist<NV, true>(v, wl, spl, sl, key, hist);
@@ -155,9 +186,10 @@ __device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[NV], int need, 
         if (!radix_find(hist, need, bin, cb)) break;
         const uint32_t blo = wl + (bin << sl);
         if ((int)cb == need || sl == 0) return ((uint64_t)key << 32) | blo;
-        spl = (1u << sl) - 1u;
+        const uint32_t top = id_lo + id_span - blo, width = (1u << sl) - 1u;
+        spl = width < top ? width : top;
         wl = blo;
-        sl -= 8;
+        sl = sl > 8 ? sl - 8 : 0u;
     }
     return ((uint64_t)key << 32) | wl;
 }
@@ -460,7 +492,8 @@ void topk_rows_stream_kernel(
                 }
                 lb = wave_min32(m1) + 1u;
             }
-            T0 = wave_kth<E + ES>(v, k, lb, hist);
+            // low words of the piece's entries: 2^32-1-col for col in [a, b)
+            T0 = wave_kth<E + ES>(v, k, lb, 0xFFFFFFFFu - (uint32_t)(b - 1), (uint32_t)(b - 1 - a), hist);
         }
         int base = 0;
         uint32_t kmin = 0xFFFFFFFFu;
@@ -737,7 +770,7 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
             bool ties;
             uint32_t ntie;
             radix_levels(sm, visit, need, wlo, span, sh, whi, thr_gt, ties, tie_key, ntie);
-            if (ties) col_cut = tie_cut(sm, visit, tie_key, ntie, need);
+            if (ties) col_cut = tie_cut(sm, visit, tie_key, ntie, need, (uint32_t)(cols - 1));
         }
     }
     auto selected = [&](uint32_t kk, uint32_t c) {
