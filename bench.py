@@ -384,10 +384,17 @@ def secondary(torch, rts, datagen, steps, warmup):
                            "rank_skewed_push_us_per_rank": t_push * 1e6}
     del x16, local, lk, recv
     x32 = torch.from_numpy(ranks32).cuda()
-    del ranks32
     pairs = torch.empty((W, R, K, 2), dtype=torch.int32, device="cuda")
     for r in range(W):
         rts.pack_pairs(x32[r], rts.topk_rows(x32[r], K), r, W, out=pairs[r])
+    # A rank's local top-2048 (the pair merge's producer), fp32 and bf16.
+    lk2 = torch.empty((R, K), dtype=torch.int32, device="cuda")
+    _, t_l32 = time_calls(lambda: rts.topk_rows(x32[0], K, out=lk2), steps, warmup, torch)
+    x16 = torch.from_numpy(datagen.bf16_bits(ranks32[0]).view(np.int16)).cuda().view(torch.bfloat16)
+    del ranks32
+    _, t_l16 = time_calls(lambda: rts.topk_rows(x16, K, out=lk2), steps, warmup, torch)
+    del x16, lk2
+    log(f"local top-2048 per rank: f32 {t_l32 * 1e6:.1f} us, bf16 {t_l16 * 1e6:.1f} us")
     pid = torch.empty((R, K), dtype=torch.int32, device="cuda")
     _, t_pairs = time_calls(lambda: rts.merge_select_pairs_rank_major(pairs, K, out=pid), steps,
                             warmup, torch)
@@ -408,18 +415,33 @@ def secondary(torch, rts, datagen, steps, warmup):
                           "row_major_select_us": t_pairs_rm * 1e6,
                           "reorder_copy_us": t_pcopy * 1e6,
                           "reorder_copy_plus_row_major_select_us": (t_pcopy + t_pairs_rm) * 1e6,
-                          "row_major_ids_identical": bool(torch.equal(pid_rm, pid))}
+                          "row_major_ids_identical": bool(torch.equal(pid_rm, pid)),
+                          "local_top2048_f32_us_per_rank": t_l32 * 1e6,
+                          "local_top2048_bf16_us_per_rank": t_l16 * 1e6}
     return res
 
 
 COUNTER_WORKLOADS = ("tiny", "prefill", "ties", "long", "decode", "robust", "robust_plus100",
-                     "robust_scale1e8", "verylong", "verylong_bf16", "merge_packed", "merge_pairs")
+                     "robust_scale1e8", "verylong", "verylong_bf16", "merge_packed", "merge_pairs",
+                     "local_top384_bf16", "local_top2048_f32", "local_top2048_bf16")
 
 
 def counters_run(name, torch, rts, datagen, calls=3):
     """Only the measured call of one workload, `calls` times (for rocprofv3 --pmc runs)."""
     import numpy as np
-    if name in ("merge_packed", "merge_pairs"):
+    if name.startswith("local_top"):
+        # one rank of the merge workload: [6710, 16384]
+        k = int(name[len("local_top"):].split("_")[0])
+        g = datagen.merge_global()
+        r0 = np.ascontiguousarray(g[:, 0::datagen.MERGE_WORLD])
+        del g
+        if name.endswith("_bf16"):
+            x = torch.from_numpy(datagen.bf16_bits(r0).view(np.int16)).cuda().view(torch.bfloat16)
+        else:
+            x = torch.from_numpy(r0).cuda()
+        out = torch.empty((r0.shape[0], k), dtype=torch.int32, device="cuda")
+        op = lambda: rts.topk_rows(x, k, out=out)
+    elif name in ("merge_packed", "merge_pairs"):
         W, R, N, K = datagen.MERGE_WORLD, datagen.MERGE_ROWS, datagen.MERGE_N, datagen.MERGE_K
         g = datagen.merge_global()
         ranks32 = datagen.rank_slices(g, W)

@@ -91,6 +91,9 @@ size_t topk_rows_workspace_size(int dtype, int64_t rows, int64_t cols, int32_t k
  * Errors: RTS_EINVAL (bad sizes/strides/pointers/dtype/alignment),
  *         RTS_EUNSUPPORTED (k > 2048, cols >= 2^31), RTS_EWORKSPACE, RTS_EHIP.
  */
+/* `dtype` is a plain int holding an rts_dtype value (RTS_F32 or RTS_BF16), so
+ * the symbol keeps one fixed C signature for foreign-function callers; any
+ * other value is RTS_EINVAL. */
 int topk_rows(const void* logits, int dtype, int64_t rows, int64_t cols, int64_t ld_logits,
               const int32_t* row_ends, int32_t k, int32_t* out_idx, int64_t ld_out,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -161,6 +164,9 @@ int pack_candidates(const uint16_t* logits_bf16, int64_t rows, int64_t cols, int
  *           exact.
  * Candidates are expected to have distinct gids; with repeated words the
  * output stays in bounds and deterministic but is not specified further.
+ * Limits are wider than the kernels page's (which takes k in {512, 1024,
+ * 2048} and n < k without its second-round state): any k in [1, 2048] and
+ * any n, since sat_word tells the caller whether round 1 was exact.
  * Errors: RTS_EINVAL, RTS_EUNSUPPORTED, RTS_EHIP.
  */
 int merge_select_rank_major(const int32_t* gathered, int32_t world, int64_t rows, int32_t n,
