@@ -338,38 +338,53 @@ __device__ __forceinline__ bool radix_find(const uint32_t* hist, int& need, uint
 }
 
 // ---------------------------------------------------------------------------
-// Wave-private 256-bin histogram in kStripes lane-striped copies: lane l
-// counts into copy l % kStripes, so lanes that share a bin mostly hit
-// different addresses.  Copies are kStripeStride words apart (16-byte
-// aligned, each copy's banks shifted by 4).
+// Wave-private 256-bin histogram in NS lane-striped copies: lane l counts
+// into copy l % NS, so lanes that share a bin mostly hit different
+// addresses.  Copies are kStripeStride words apart (16-byte aligned, each
+// copy's banks shifted by 4).
 // ---------------------------------------------------------------------------
 constexpr int kStripes = 4;
 constexpr int kStripeStride = 260;
 constexpr int kStripedWords = kStripes * kStripeStride;
 
-__device__ __forceinline__ void striped_clear(uint32_t* hist) {
-    const int lane = lane_id();  // lane l clears bins 16(l%16) .. +15 of copy l/16
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    u32x4_t* p = reinterpret_cast<u32x4_t*>(hist + (lane >> 4) * kStripeStride + 16 * (lane & 15));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = u32x4_t{0u, 0u, 0u, 0u};
+// Stripe count that fits `words` words of LDS: a power of two, at most 8.
+constexpr int stripes_fitting(int words) {
+    return words >= 8 * kStripeStride ? 8 : words >= 4 * kStripeStride ? 4 : words >= 2 * kStripeStride ? 2 : 1;
 }
 
+// Each store covers one whole copy (64 lanes x 16 B).
+template <int NS = kStripes>
+__device__ __forceinline__ void striped_clear(uint32_t* hist) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const int lane = lane_id();
+#pragma unroll
+    for (int c = 0; c < NS; ++c)
+        *reinterpret_cast<u32x4_t*>(hist + c * kStripeStride + 4 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+}
+
+// This lane's copy.
+template <int NS = kStripes>
+__device__ __forceinline__ uint32_t* striped_copy(uint32_t* hist) {
+    return hist + (lane_id() & (NS - 1)) * kStripeStride;
+}
+
+template <int NS = kStripes>
 __device__ __forceinline__ void striped_add(uint32_t* hist, uint32_t bin) {
-    __hip_atomic_fetch_add(&hist[(lane_id() & (kStripes - 1)) * kStripeStride + bin], 1u,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    __hip_atomic_fetch_add(&striped_copy<NS>(hist)[bin], 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WAVEFRONT);
 }
 
 // radix_find over the sum of the striped copies.
+template <int NS = kStripes>
 __device__ __forceinline__ bool striped_find(const uint32_t* hist, int& need, uint32_t& bin,
                                              uint32_t& cb) {
     const int lane = lane_id();
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     // bins 252-4l .. 255-4l: one 16-byte read per copy, the copies summed
-    // one after the other (a real loop: the caller holds many registers)
+    // one after the other (a real loop: the callers hold many registers)
     u32x4_t acc = *reinterpret_cast<const u32x4_t*>(hist + 252 - 4 * lane);
 #pragma unroll 1
-    for (int s = 1; s < kStripes; ++s)
+    for (int s = 1; s < NS; ++s)
         acc += *reinterpret_cast<const u32x4_t*>(hist + s * kStripeStride + 252 - 4 * lane);
     const uint32_t c[4] = {acc[3], acc[2], acc[1], acc[0]};
     return radix_find_counts(c, need, bin, cb);

@@ -88,7 +88,9 @@ __device__ __forceinline__ void unpack(typename RowTraits<BF16>::vec v, uint32_t
 // Exact k-th composite of a wave-held set (the compaction's select).
 //
 // A window [w, w + span] of one 32-bit word is cut into 256 bins of width
-// 2^s, counted in wave-private LDS.  The bin where the count from the top
+// 2^s, counted in wave-private LDS (the wave's stage memory, whose entries
+// are in registers by then; NS0 lane-striped copies for the first level,
+// one copy after).  The bin where the count from the top
 // reaches `need` becomes the next window (s drops by 8), first on the key
 // word, then, when the k-th key is tied, on the low (id) word of the entries
 // with that key.  Bins are sized from the known range, so no level needs a
@@ -97,22 +99,21 @@ __device__ __forceinline__ void unpack(typename RowTraits<BF16>::vec v, uint32_t
 // ---------------------------------------------------------------------------
 
 // Counts the entries whose word x = word - w lies in [0, span] into bin
-// x >> s.  LO: the word is the low word, and only entries whose key equals
-// key_eq count (a tie level).  Empty entries (0) never count: their key is 0,
-// below every window.
-template <int NV, bool LO>
+// x >> s, in NS lane-striped copies.  LO: the word is the low word, and only
+// entries whose key equals key_eq count (a tie level).  Empty entries (0)
+// never count: their key is 0, below every window.
+template <int NV, bool LO, int NS>
 __device__ __forceinline__ void radix_hist(const uint64_t (&v)[NV], uint32_t w, uint32_t span,
                                            uint32_t s, uint32_t key_eq, uint32_t* hist) {
-    const int lane = lane_id();
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    *reinterpret_cast<u32x4_t*>(hist + 4 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+    striped_clear<NS>(hist);
     wave_lds_sync();
+    uint32_t* mine = striped_copy<NS>(hist);
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
         const uint32_t hi = (uint32_t)(v[r] >> 32);
         const uint32_t x = (LO ? (uint32_t)v[r] : hi) - w;
         const bool in = LO ? (hi == key_eq && x <= span) : x <= span;
-        if (in) __hip_atomic_fetch_add(&hist[x >> s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+        if (in) __hip_atomic_fetch_add(&mine[x >> s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
     }
     wave_lds_sync();
 }
@@ -120,7 +121,7 @@ __device__ __forceinline__ void radix_hist(const uint64_t (&v)[NV], uint32_t w, 
 // T such that exactly `need` nonzero entries of v[] are >= T (composites are
 // distinct).  Requires at least `need` nonzero entries, all with key >= lb
 // and low word in [id_lo, id_lo + id_span] (the piece's columns).
-template <int NV>
+template <int NV, int NS0>
 __device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[NV], int need, uint32_t lb,
                                              uint32_t id_lo, uint32_t id_span, uint32_t* hist) {
     uint32_t mx = 0;
@@ -136,9 +137,16 @@ __device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[NV], int need, 
     uint32_t s = bl > 8 ? (uint32_t)(bl - 8) : 0u;
 #pragma unroll 1
     for (int level = 0; level < 4; ++level) {
-        radix_hist<NV, false>(v, w, span, s, 0u, hist);
         uint32_t bin, cb;
-        if (!radix_find(hist, need, bin, cb)) return (uint64_t)w << 32;
+        bool ok;
+        if (level == 0) {
+            radix_hist<NV, false, NS0>(v, w, span, s, 0u, hist);
+            ok = striped_find<NS0>(hist, need, bin, cb);
+        } else {
+            radix_hist<NV, false, 1>(v, w, span, s, 0u, hist);
+            ok = striped_find<1>(hist, need, bin, cb);
+        }
+        if (!ok) return (uint64_t)w << 32;
         const uint32_t blo = w + (bin << s);
         if ((int)cb == need) return (uint64_t)blo << 32;
         w = blo;
@@ -181,9 +189,9 @@ __device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[NV], int need, 
     uint32_t sl = bll > 8 ? (uint32_t)(bll - 8) : 0u;
 #pragma unroll 1
     for (int level = 0; level < 4; ++level) {
-        radix_hist<NV, true>(v, wl, spl, sl, key, hist);
+        radix_hist<NV, true, 1>(v, wl, spl, sl, key, hist);
         uint32_t bin, cb;
-        if (!radix_find(hist, need, bin, cb)) break;
+        if (!striped_find<1>(hist, need, bin, cb)) break;
         const uint32_t blo = wl + (bin << sl);
         if ((int)cb == need || sl == 0) return ((uint64_t)key << 32) | blo;
         const uint32_t top = id_lo + id_span - blo, width = (1u << sl) - 1u;
@@ -208,17 +216,23 @@ void topk_rows_stream_kernel(
     constexpr int SBUF = SCAP > LP ? SCAP : LP;  // also carries the selected list into L
     static_assert(SCAP >= kChunk, "the stage must take a whole chunk");
 
-    // SBUF slots, then one slot per lane where lanes that fail the filter write.
-    __shared__ uint64_t stage_all[P][SBUF + kWave];
-    __shared__ __attribute__((aligned(16))) uint32_t hist_all[P][256];
+    // SBUF slots, then one slot per lane where lanes that fail the filter
+    // write.  A compaction first moves the staged entries to registers, so
+    // its histograms (NS lane-striped copies) reuse the stage memory.
+    __shared__ __attribute__((aligned(16))) uint64_t stage_all[P][SBUF + kWave];
     __shared__ uint32_t thr_shared;
+    // The first level of a compaction counts every entry over the whole
+    // range in play, where a concentrated or heavy-tailed distribution puts
+    // most entries into a few bins: 4 copies there; later levels see one
+    // bin's entries, spread out, and use a single copy.
+    constexpr int NS0 = stripes_fitting(2 * (SBUF + kWave)) < 4 ? stripes_fitting(2 * (SBUF + kWave)) : 4;
 
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t row = blockIdx.x / groups;
     const int g = (int)(blockIdx.x - row * groups);
     uint64_t* stage = stage_all[wave];
-    uint32_t* hist = hist_all[wave];
+    uint32_t* hist = reinterpret_cast<uint32_t*>(stage);
 
     int64_t e = row_ends ? (int64_t)row_ends[row] : cols;
     e = e < 0 ? 0 : (e > cols ? cols : e);
@@ -364,17 +378,24 @@ void topk_rows_stream_kernel(
         if (cnt > SCAP - kChunk &&
             cnt + (int)(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3])) > SCAP)
             return false;
-        uint32_t sa = stage_base + (uint32_t)cnt * 8u;
-        asm volatile("" : "+s"(sa));  // keep the base whole: one v_lshl_add per slot
+        // The running slot count stays in a VGPR and advances with v_bcnt (the
+        // lane's slot comes from v_mbcnt on it), so an append costs no SALU
+        // beyond the test of its mask.
+        uint32_t off = (uint32_t)cnt;
+        asm volatile("" : "+v"(off));
 #pragma unroll
         for (int c = 0; c < kVec; ++c) {
             if (m[c]) {
-                const uint32_t a = select_by_mask(m[c], sa + mbcnt64(m[c]) * 8u, sink);
+                const uint32_t lo = (uint32_t)m[c], hi = (uint32_t)(m[c] >> 32);
+                const uint32_t pos = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, off));
+                const uint32_t a = select_by_mask(m[c], stage_base + pos * 8u, sink);
                 lds_store2(a, idn - (uint32_t)c, bits[c]);
-                sa += (uint32_t)__popcll(m[c]) * 8u;
+                uint32_t t;
+                asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(t) : "s"(lo), "v"(off));
+                asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(off) : "s"(hi), "v"(t));
             }
         }
-        cnt = (int)((sa - stage_base) >> 3);
+        cnt = __builtin_amdgcn_readfirstlane((int)off);
         return true;
     };
 
@@ -493,7 +514,8 @@ void topk_rows_stream_kernel(
                 lb = wave_min32(m1) + 1u;
             }
             // low words of the piece's entries: 2^32-1-col for col in [a, b)
-            T0 = wave_kth<E + ES>(v, k, lb, 0xFFFFFFFFu - (uint32_t)(b - 1), (uint32_t)(b - 1 - a), hist);
+            wave_lds_sync();  // the stage's entries are in v[]: its memory holds the histograms
+            T0 = wave_kth<E + ES, NS0>(v, k, lb, 0xFFFFFFFFu - (uint32_t)(b - 1), (uint32_t)(b - 1 - a), hist);
         }
         int base = 0;
         uint32_t kmin = 0xFFFFFFFFu;
