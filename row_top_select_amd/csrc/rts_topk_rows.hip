@@ -328,16 +328,28 @@ void topk_rows_stream_kernel(
     }
 
     V A[kGroup], B[kGroup];
-    // Loads group gi; past the last group every load re-reads the last chunk
-    // (just read by this wave, an L2 hit), so the refills are unconditional
-    // and the order of outstanding loads is the same on every path.
+    // Loads group gi.  The refills are unconditional, so the order of
+    // outstanding loads is the same on every path.  Buffer loads through a
+    // resource made per group (base: the group's first chunk; size: the
+    // piece's bytes left, at most a group): the lane's byte offset sits in a
+    // VGPR set once, so a refill computes no vector address in the registers
+    // the previous group's data occupies (which made it wait for the other
+    // group's loads).  Chunks past the piece's end are out of range and read
+    // as zeros without touching memory; they are never filtered.
+    const int voff = lane * (int)sizeof(V);
     auto load_group = [&](V(&dst)[kGroup], int gi) {
+        constexpr int kGroupBytes = kGroup * kChunk * (int)sizeof(T);
+        const int left = nch - gi * kGroup;
+        const int bytes = left <= 0 ? 0 : (left >= kGroup ? kGroupBytes : left * kChunk * (int)sizeof(T));
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<V*>(cbase + (int64_t)gi * kGroup * kWave), (short)0, bytes, 0x00020000);
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
-            uint32_t c = (uint32_t)(gi * kGroup + u);
-            c = c < (uint32_t)nch ? c : (uint32_t)nch - 1u;
-            const V* gp = cbase + (uint64_t)c * kWave;  // wave-uniform
-            dst[u] = __builtin_nontemporal_load(gp + lane);
+            constexpr int kChunkBytes = kChunk * (int)sizeof(T);
+            if constexpr (BF16)
+                dst[u] = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff + u * kChunkBytes, 0, 2);
+            else
+                dst[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + u * kChunkBytes, 0, 2);
         }
     };
     int gi = 0;
