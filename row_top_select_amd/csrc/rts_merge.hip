@@ -714,23 +714,34 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
 
     uint32_t w[NR];
     uint32_t hb0 = 0u, hb1 = 0u;  // bit i (hb1: i - 32): the slot's plane bit (local bit 16)
+    // A rank's n/32 plane words are read one per lane (a vector load, not
+    // n/32 scalar registers per rank); slot q*64 + l takes bit l % 32 of word
+    // 2q + l/32, fetched from the lane that holds it.  A rank whose plane is
+    // all zero (local ids below 2^16, the common case) skips the fetches.
+    const int npw = n / 32;
 #pragma unroll
     for (int r = 0; r < W; ++r) {
         const int32_t* rp = gathered + lay.at(r, row) * width;
+        const uint32_t pw = lane < npw ? (uint32_t)rp[n + lane] : 0u;
 #pragma unroll
         for (int q = 0; q < QN; ++q) {
             const int i = r * QN + q;
             // Only the last register of a rank can reach past n (n % 64 == 32).
             const bool in = q < QN - 1 || q * kWave + lane < n;
             const uint32_t word = (uint32_t)rp[in ? q * kWave + lane : 0];
-            // Plane words 2q and 2q+1 cover slots q*64 .. q*64+63: bit `lane`
-            // of their 64-bit concatenation (one uniform load).
-            uint64_t plane = (uint32_t)rp[n + 2 * q];
-            if (q < QN - 1 || q * kWave + 32 < n) plane |= (uint64_t)(uint32_t)rp[n + 2 * q + 1] << 32;
             w[i] = in ? word : 0u;
-            const uint32_t bit = in ? (uint32_t)(plane >> lane) & 1u : 0u;
-            if (i < 32) hb0 |= bit << i;
-            else hb1 |= bit << (i - 32);
+        }
+        if (__ballot(pw != 0u)) {
+#pragma unroll
+            for (int q = 0; q < QN; ++q) {
+                const int i = r * QN + q;
+                const bool in = q < QN - 1 || q * kWave + lane < n;
+                const int src = 2 * q + (lane >> 5);
+                const uint32_t pword = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)pw);
+                const uint32_t bit = in ? (pword >> (lane & 31)) & 1u : 0u;
+                if (i < 32) hb0 |= bit << i;
+                else hb1 |= bit << (i - 32);
+            }
         }
     }
     auto hibit = [&](int i) -> uint32_t { return i < 32 ? (hb0 >> i) & 1u : (hb1 >> (i - 32)) & 1u; };
