@@ -638,6 +638,7 @@ struct BlockRowSmem {
     uint32_t bc[4];
     uint32_t tied[kWave];
     uint32_t ntied;
+    uint32_t nsel;
     uint32_t red[NW][4];
 };
 
@@ -652,7 +653,9 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
     constexpr int LS = S * NW;    // sort slots of the workgroup (>= k)
     static_assert(KPT % 4 == 0, "keys come in groups of four");
     __shared__ BlockRowSmem<NW> sm;
+    constexpr int CAPL = 128;     // boundary-bin list entries per wave
     __shared__ uint64_t buf[LS];
+    __shared__ uint64_t lst[NW][CAPL];
     const int t = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
     const int64_t row = blockIdx.x;
@@ -661,7 +664,10 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
     const T* rowp = reinterpret_cast<const T*>(xv) + row * ld;
 
     for (int q = t; q < kLevelCopies * kLevelStride; q += NT) (&sm.hist[0][0])[q] = 0u;
-    if (t == 0) sm.ntied = 0u;
+    if (t == 0) {
+        sm.ntied = 0u;
+        sm.nsel = 0u;
+    }
 
     // Column of key i, from the thread's base column 4t.  Each pass takes an
     // opaque copy of the base, so the compiler cannot keep KPT column values
@@ -736,6 +742,10 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
 
     // Selected: key > thr_gt, or key == tie_key and column <= col_cut.
     uint32_t thr_gt = 0u, tie_key = 0u, col_cut = 0u;
+    auto selected = [&](uint32_t kk, uint32_t c) {
+        return kk != 0u && (kk > thr_gt || (kk == tie_key && c <= col_cut));
+    };
+    bool written = false;  // the k selected composites are in buf already
     if (nv > (uint32_t)k) {
         auto visit = [&](auto f) __attribute__((always_inline)) {
             const uint32_t cb = col_base();
@@ -758,42 +768,103 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
                 const float tb = (float_of_key32(kk) - lo) * scale;  // in [0, 256]
                 return (uint32_t)(tb < 255.0f ? tb : 255.0f);
             };
+            // Empty slots count into the padding word 256, which no level reads.
 #pragma unroll
             for (int i = 0; i < KPT; ++i)
-                if (key[i] != 0u)
-                    __hip_atomic_fetch_add(&sm.hist[lane & (kLevelCopies - 1)][vbin(key[i])], 1u,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(&sm.hist[lane & (kLevelCopies - 1)][key[i] != 0u ? vbin(key[i]) : 256u],
+                                       1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             uint32_t bin, cbin;
             if (level_hist_find(sm, need, bin, cbin)) {
-                // Key range of the boundary bin.
-                uint32_t bmn = 0xFFFFFFFFu, bmx = 0u;
+                // One pass over the keys: a key in a bin above the boundary bin
+                // is selected (a bit of amask; written once the waves' offsets
+                // are known), a key in the boundary bin goes to the wave's list
+                // (at most CAPL), where the later levels and the tie rule
+                // resolve it.  The boundary bin's key range comes along.
+                uint32_t amask = 0u, na = 0u, nl = 0u, lmn = 0xFFFFFFFFu, lmx = 0u;
+                const uint32_t cbl = col_base();
 #pragma unroll
                 for (int i = 0; i < KPT; ++i) {
-                    const bool in = key[i] != 0u && vbin(key[i]) == bin;
-                    bmn = in && key[i] < bmn ? key[i] : bmn;
-                    bmx = in && key[i] > bmx ? key[i] : bmx;
+                    const uint32_t vb = vbin(key[i]);
+                    const bool ok = key[i] != 0u;
+                    const bool above = ok && vb > bin;
+                    const bool in = ok && vb == bin;
+                    amask |= above ? (1u << i) : 0u;
+                    na += (uint32_t)__popcll(__ballot(above));
+                    const uint64_t m = __ballot(in);
+                    const uint32_t pos = nl + mbcnt64(m);
+                    if (in && pos < (uint32_t)CAPL) lst[wave][pos] = composite(key[i], col_at(cbl, i));
+                    lmn = in && key[i] < lmn ? key[i] : lmn;
+                    lmx = in && key[i] > lmx ? key[i] : lmx;
+                    nl += (uint32_t)__popcll(m);
                 }
-                bmn = wave_min32(bmn);
-                bmx = wave_max32(bmx);
+                lmn = wave_min32(lmn);
+                lmx = wave_max32(lmx);
                 if (lane == 0) {
-                    sm.red[wave][1] = bmn;
-                    sm.red[wave][2] = bmx;
+                    sm.red[wave][0] = na;
+                    sm.red[wave][1] = nl;
+                    sm.red[wave][2] = lmn;
+                    sm.red[wave][3] = lmx;
                 }
                 lds_barrier();
-                bmn = 0xFFFFFFFFu;
-                bmx = 0u;
+                uint32_t aoff = 0u, atot = 0u, bmn = 0xFFFFFFFFu, bmx = 0u;
+                bool fits = true;
 #pragma unroll
                 for (int w = 0; w < NW; ++w) {
-                    bmn = sm.red[w][1] < bmn ? sm.red[w][1] : bmn;
-                    bmx = sm.red[w][2] > bmx ? sm.red[w][2] : bmx;
+                    aoff += w < wave ? sm.red[w][0] : 0u;
+                    atot += sm.red[w][0];
+                    fits = fits && sm.red[w][1] <= (uint32_t)CAPL;
+                    bmn = sm.red[w][2] < bmn ? sm.red[w][2] : bmn;
+                    bmx = sm.red[w][3] > bmx ? sm.red[w][3] : bmx;
                 }
-                lds_barrier();
-                if ((int)cbin == need) {  // the whole bin is taken: keys >= its smallest
-                    thr_gt = bmn - 1u;
+                if ((int)cbin == need) thr_gt = bmn - 1u;  // the whole bin is taken: keys >= its smallest
+                if (fits) {
+                    if ((int)cbin != need) {
+                        const uint32_t mine = nl;  // this wave's list entries
+                        auto visit_list = [&](auto f) __attribute__((always_inline)) {
+                            for (uint32_t p = (uint32_t)lane; p < mine; p += kWave) {
+                                const uint64_t c = lst[wave][p];
+                                f((uint32_t)(c >> 32), composite_id(c));
+                            }
+                        };
+                        const uint32_t span = bmx - bmn;
+                        const int bl = span ? 32 - __clz((int)span) : 0;
+                        const uint32_t sh = bl > 8 ? (uint32_t)(bl - 8) : 0u;
+                        bool ties;
+                        uint32_t ntie;
+                        radix_levels(sm, visit_list, need, bmn, span, sh, bmx, thr_gt, ties, tie_key, ntie);
+                        if (ties) col_cut = tie_cut(sm, visit_list, tie_key, ntie, need, (uint32_t)(cols - 1));
+                    }
+                    // The selected: keys above the boundary bin at this wave's
+                    // offset, then the list's selected after all of those (any
+                    // order: the sort below fixes it), then empty slots.
+                    const uint32_t cbw = col_base();
+#pragma unroll
+                    for (int i = 0; i < KPT; ++i) {
+                        const bool a = ((amask >> i) & 1u) != 0u;
+                        const uint64_t m = __ballot(a);
+                        const uint32_t pos = aoff + mbcnt64(m);
+                        if (a) buf[pos] = composite(key[i], col_at(cbw, i));
+                        aoff += (uint32_t)__popcll(m);
+                    }
+                    for (uint32_t p = (uint32_t)lane; p < nl; p += kWave) {
+                        const uint64_t c = lst[wave][p];
+                        if (selected((uint32_t)(c >> 32), composite_id(c))) {
+                            const uint32_t q = __hip_atomic_fetch_add(&sm.nsel, 1u, __ATOMIC_RELAXED,
+                                                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+                            buf[atot + q] = c;
+                        }
+                    }
+                    for (int p = k + t; p < LS; p += NT) buf[p] = 0ull;
+                    written = true;
                     done = true;
                 } else {
-                    wlo = bmn;
-                    whi = bmx;
+                    lds_barrier();  // sm.red is rewritten below
+                    if ((int)cbin == need) {
+                        done = true;
+                    } else {
+                        wlo = bmn;
+                        whi = bmx;
+                    }
                 }
             }
         }
@@ -807,34 +878,33 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
             if (ties) col_cut = tie_cut(sm, visit, tie_key, ntie, need, (uint32_t)(cols - 1));
         }
     }
-    auto selected = [&](uint32_t kk, uint32_t c) {
-        return kk != 0u && (kk > thr_gt || (kk == tie_key && c <= col_cut));
-    };
 
-    // The selected composites into LDS (any order), empty slots after them.
-    uint32_t cnt = 0;
-    uint32_t cb = col_base();
+    if (!written) {
+        // The selected composites into LDS (any order), empty slots after them.
+        uint32_t cnt = 0;
+        uint32_t cb = col_base();
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) cnt += (uint32_t)__popcll(__ballot(selected(key[i], col_at(cb, i))));
-    if (lane == 0) sm.red[wave][3] = cnt;
-    lds_barrier();
-    uint32_t off = 0, total = 0;
+        for (int i = 0; i < KPT; ++i) cnt += (uint32_t)__popcll(__ballot(selected(key[i], col_at(cb, i))));
+        if (lane == 0) sm.red[wave][3] = cnt;
+        lds_barrier();
+        uint32_t off = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        off += w < wave ? sm.red[w][3] : 0u;
-        total += sm.red[w][3];
+        for (int w = 0; w < NW; ++w) {
+            off += w < wave ? sm.red[w][3] : 0u;
+            total += sm.red[w][3];
+        }
+        cb = col_base();
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const uint32_t c = col_at(cb, i);
+            const bool sel = selected(key[i], c);
+            const uint64_t m = __ballot(sel);
+            const uint32_t pos = off + mbcnt64(m);
+            if (sel && pos < (uint32_t)LS) buf[pos] = composite(key[i], c);
+            off += (uint32_t)__popcll(m);
+        }
+        for (int p = (int)(total < (uint32_t)LS ? total : (uint32_t)LS) + t; p < LS; p += NT) buf[p] = 0ull;
     }
-    cb = col_base();
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const uint32_t c = col_at(cb, i);
-        const bool sel = selected(key[i], c);
-        const uint64_t m = __ballot(sel);
-        const uint32_t pos = off + mbcnt64(m);
-        if (sel && pos < (uint32_t)LS) buf[pos] = composite(key[i], c);
-        off += (uint32_t)__popcll(m);
-    }
-    for (int p = (int)(total < (uint32_t)LS ? total : (uint32_t)LS) + t; p < LS; p += NT) buf[p] = 0ull;
     lds_barrier();
 
     // Descending sort of the LS slots; element i = wave * S + lane * E + r.
