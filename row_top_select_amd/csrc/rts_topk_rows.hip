@@ -639,6 +639,7 @@ struct BlockRowSmem {
     uint32_t tied[kWave];
     uint32_t ntied;
     uint32_t nsel;
+    uint32_t nlist[NW];
     uint32_t red[NW][4];
 };
 
@@ -668,6 +669,7 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
         sm.ntied = 0u;
         sm.nsel = 0u;
     }
+    if (t < NW) sm.nlist[t] = 0u;
 
     // Column of key i, from the thread's base column 4t.  Each pass takes an
     // opaque copy of the base, so the compiler cannot keep KPT column values
@@ -680,32 +682,46 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
     auto col_at = [](uint32_t base, int i) -> uint32_t {
         return base + (uint32_t)(4 * (i >> 2) * NT + (i & 3));
     };
-    // Every whole group of four inside the row end is one vector load, all
-    // issued before any is used; a group cut by the row end, or every group
-    // of a row not aligned to a vector, is read element by element.
+    // Loads through a buffer resource over the row's valid bytes: a lane's
+    // offset is one register and the group's offset a constant, and reads
+    // past the row end return zero without touching memory.  Every group is
+    // one vector load, all issued before any is used; the group cut by the
+    // row end, or every group of a row not aligned to a vector, is read
+    // element by element.
+    const int ei = (int)e;  // e <= cols <= 64 * 8 * KPT
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(rowp), (short)0, ei * (int)sizeof(T), 0x00020000);
     const bool vec_ok = (reinterpret_cast<uintptr_t>(rowp) % sizeof(V)) == 0;
     uint32_t key[KPT];
     {
         V raw[KPT / 4];
-        const int64_t t4 = 4 * (int64_t)t;
+        const int voff = t * (int)sizeof(V);
 #pragma unroll
         for (int g = 0; g < KPT / 4; ++g) {
-            const int64_t c0 = (int64_t)g * NT * 4 + t4;
-            raw[g] = V{};
-            if (vec_ok && c0 + 4 <= e) raw[g] = __builtin_nontemporal_load(reinterpret_cast<const V*>(rowp + c0));
+            constexpr int kGroupStride = NT * (int)sizeof(V);
+            if constexpr (BF16)
+                raw[g] = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, g * kGroupStride, 2);
+            else
+                raw[g] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, g * kGroupStride, 2);
         }
+        const int t4 = (int)col_base();
 #pragma unroll
         for (int g = 0; g < KPT / 4; ++g) {
-            const int64_t c0 = (int64_t)g * NT * 4 + t4;
+            const int c0 = g * NT * 4 + t4;
             uint32_t bits[4];
             unpack<BF16>(raw[g], bits);
-            if (c0 < e && (!vec_ok || c0 + 4 > e)) {
+            if (c0 < ei && (!vec_ok || c0 + 4 > ei)) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bits[j] = c0 + j < e ? load_bits<BF16>(rowp + c0 + j) : 0u;
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (BF16)
+                        bits[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, (c0 + j) * 2, 0, 0) << 16;
+                    else
+                        bits[j] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (c0 + j) * 4, 0, 0);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bool ok = c0 + j < e && !f32_bits_is_nan(bits[j]);
+                const bool ok = c0 + j < ei && !f32_bits_is_nan(bits[j]);
                 key[4 * g + j] = ok ? key32_of_bits(bits[j]) : 0u;
             }
         }
@@ -713,14 +729,16 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
 
     // Valid count and key range (every valid key is >= key32(-inf) > 0; the
     // minimum is taken over key - 1, which sends empty slots to the top).
+    // Per-lane figures, then the wave's, then lane w < NW combines wave w's.
     uint32_t nv = 0, mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        nv += (uint32_t)__popcll(__ballot(key[i] != 0u));
+        nv += key[i] != 0u ? 1u : 0u;
         const uint32_t km1 = key[i] - 1u;
         mn = km1 < mn ? km1 : mn;
         mx = key[i] > mx ? key[i] : mx;
     }
+    nv = wave_sum32(nv);
     mn = wave_min32(mn);
     mx = wave_max32(mx);
     if (lane == 0) {
@@ -729,14 +747,11 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
         sm.red[wave][2] = mx;
     }
     lds_barrier();
-    nv = 0;
-    mn = 0xFFFFFFFFu;
-    mx = 0u;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        nv += sm.red[w][0];
-        mn = sm.red[w][1] < mn ? sm.red[w][1] : mn;
-        mx = sm.red[w][2] > mx ? sm.red[w][2] : mx;
+    {
+        const bool wl = lane < NW;
+        nv = wave_sum32(wl ? sm.red[lane][0] : 0u);
+        mn = wave_min32(wl ? sm.red[lane][1] : 0xFFFFFFFFu);
+        mx = wave_max32(wl ? sm.red[lane][2] : 0u);
     }
     mn += 1u;
 
@@ -776,45 +791,59 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
             uint32_t bin, cbin;
             if (level_hist_find(sm, need, bin, cbin)) {
                 // One pass over the keys: a key in a bin above the boundary bin
-                // is selected (a bit of amask; written once the waves' offsets
-                // are known), a key in the boundary bin goes to the wave's list
-                // (at most CAPL), where the later levels and the tie rule
+                // is selected (a bit of amask, written once the offsets are
+                // known), a key in the boundary bin goes to the wave's list (at
+                // most CAPL; slots from an LDS counter, as the list's order
+                // does not matter), where the later levels and the tie rule
                 // resolve it.  The boundary bin's key range comes along.
-                uint32_t amask = 0u, na = 0u, nl = 0u, lmn = 0xFFFFFFFFu, lmx = 0u;
+                // Counts stay per lane: no wave masks are held per key.
+                uint32_t amask = 0u, na = 0u, lmn = 0xFFFFFFFFu, lmx = 0u;
                 const uint32_t cbl = col_base();
+                // The bins again from an opaque copy of the offset: otherwise
+                // the compiler keeps every key's bin from the histogram pass
+                // (a register per key).
+                float lo2 = lo;
+                asm volatile("" : "+v"(lo2));
 #pragma unroll
                 for (int i = 0; i < KPT; ++i) {
-                    const uint32_t vb = vbin(key[i]);
+                    const float tb = (float_of_key32(key[i]) - lo2) * scale;
+                    const uint32_t vb = (uint32_t)(tb < 255.0f ? tb : 255.0f);
                     const bool ok = key[i] != 0u;
                     const bool above = ok && vb > bin;
-                    const bool in = ok && vb == bin;
                     amask |= above ? (1u << i) : 0u;
-                    na += (uint32_t)__popcll(__ballot(above));
-                    const uint64_t m = __ballot(in);
-                    const uint32_t pos = nl + mbcnt64(m);
-                    if (in && pos < (uint32_t)CAPL) lst[wave][pos] = composite(key[i], col_at(cbl, i));
-                    lmn = in && key[i] < lmn ? key[i] : lmn;
-                    lmx = in && key[i] > lmx ? key[i] : lmx;
-                    nl += (uint32_t)__popcll(m);
+                    na += above ? 1u : 0u;
+                    if (ok && vb == bin) {
+                        const uint32_t pos = __hip_atomic_fetch_add(&sm.nlist[wave], 1u, __ATOMIC_RELAXED,
+                                                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+                        if (pos < (uint32_t)CAPL) lst[wave][pos] = composite(key[i], col_at(cbl, i));
+                        lmn = key[i] < lmn ? key[i] : lmn;
+                        lmx = key[i] > lmx ? key[i] : lmx;
+                    }
                 }
+                const uint32_t na_incl = wave_incl_scan32(na);
+                const uint32_t na_wave = (uint32_t)__builtin_amdgcn_readlane((int)na_incl, kWave - 1);
                 lmn = wave_min32(lmn);
                 lmx = wave_max32(lmx);
                 if (lane == 0) {
-                    sm.red[wave][0] = na;
-                    sm.red[wave][1] = nl;
+                    sm.red[wave][0] = na_wave;
                     sm.red[wave][2] = lmn;
                     sm.red[wave][3] = lmx;
                 }
                 lds_barrier();
-                uint32_t aoff = 0u, atot = 0u, bmn = 0xFFFFFFFFu, bmx = 0u;
-                bool fits = true;
-#pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    aoff += w < wave ? sm.red[w][0] : 0u;
-                    atot += sm.red[w][0];
-                    fits = fits && sm.red[w][1] <= (uint32_t)CAPL;
-                    bmn = sm.red[w][2] < bmn ? sm.red[w][2] : bmn;
-                    bmx = sm.red[w][3] > bmx ? sm.red[w][3] : bmx;
+                // Lane w < NW takes wave w's figures; wave reductions combine
+                // them (fewer registers than every wave's figures in each lane).
+                const uint32_t nl = sm.nlist[wave];
+                uint32_t aoff, atot, bmn, bmx;
+                bool fits;
+                {
+                    const bool wl = lane < NW;
+                    const uint32_t wa = wl ? sm.red[lane][0] : 0u;
+                    const uint32_t incl = wave_incl_scan32(wa);
+                    atot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+                    aoff = wave == 0 ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)incl, wave - 1);
+                    fits = wave_max32(wl ? sm.nlist[lane] : 0u) <= (uint32_t)CAPL;
+                    bmn = wave_min32(wl ? sm.red[lane][2] : 0xFFFFFFFFu);
+                    bmx = wave_max32(wl ? sm.red[lane][3] : 0u);
                 }
                 if ((int)cbin == need) thr_gt = bmn - 1u;  // the whole bin is taken: keys >= its smallest
                 if (fits) {
@@ -838,13 +867,12 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
                     // offset, then the list's selected after all of those (any
                     // order: the sort below fixes it), then empty slots.
                     const uint32_t cbw = col_base();
+                    uint32_t q = aoff + na_incl - na;  // this lane's first slot
 #pragma unroll
                     for (int i = 0; i < KPT; ++i) {
-                        const bool a = ((amask >> i) & 1u) != 0u;
-                        const uint64_t m = __ballot(a);
-                        const uint32_t pos = aoff + mbcnt64(m);
-                        if (a) buf[pos] = composite(key[i], col_at(cbw, i));
-                        aoff += (uint32_t)__popcll(m);
+                        const uint32_t a = (amask >> i) & 1u;
+                        if (a) buf[q] = composite(key[i], col_at(cbw, i));
+                        q += a;
                     }
                     for (uint32_t p = (uint32_t)lane; p < nl; p += kWave) {
                         const uint64_t c = lst[wave][p];
@@ -887,12 +915,9 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
         for (int i = 0; i < KPT; ++i) cnt += (uint32_t)__popcll(__ballot(selected(key[i], col_at(cb, i))));
         if (lane == 0) sm.red[wave][3] = cnt;
         lds_barrier();
-        uint32_t off = 0, total = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            off += w < wave ? sm.red[w][3] : 0u;
-            total += sm.red[w][3];
-        }
+        const uint32_t incl = wave_incl_scan32(lane < NW ? sm.red[lane][3] : 0u);
+        uint32_t off = wave == 0 ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)incl, wave - 1);
+        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
         cb = col_base();
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
