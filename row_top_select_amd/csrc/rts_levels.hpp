@@ -12,6 +12,8 @@
 // hist[kLevelCopies][kLevelStride], bins[256], bc[4], tied[64] and ntied.
 #pragma once
 
+#include <type_traits>
+
 #include "rts_device.hpp"
 
 namespace rts {
@@ -37,26 +39,54 @@ __device__ __forceinline__ void level_hist_add(Smem& sm, uint32_t key, uint32_t 
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// All threads, after their level_hist_add calls: sums (and clears) the copies,
-// then wave 0 finds the bin where the count from the top reaches need.
-// Returns (uniform) ok, the bin and its count, and lowers need by the count
-// above the bin.
+// Smem types that set kWave0Find = true take level_hist_find's two-barrier
+// form (wave 0 alone sums the copies); the others the four-barrier form
+// (every thread sums a few bins), which holds fewer registers in wave 0.
+template <typename S, typename = void>
+struct Wave0Find : std::false_type {};
+template <typename S>
+struct Wave0Find<S, std::void_t<decltype(S::kWave0Find)>> : std::integral_constant<bool, S::kWave0Find> {};
+
+// All threads, after their level_hist_add calls: sums (and clears, for the
+// next level) the copies, then wave 0 finds the bin where the count from the
+// top reaches need.  Returns (uniform) ok, the bin and its count, and lowers
+// need by the count above the bin.
 template <typename Smem>
 __device__ __forceinline__ bool level_hist_find(Smem& sm, int& need, uint32_t& bin, uint32_t& cb) {
     const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
     lds_barrier();
-    for (int b = threadIdx.x; b < 256; b += blockDim.x) {  // the block may have < 256 threads
-        uint32_t t = 0;
+    if constexpr (Wave0Find<Smem>::value) {
+        // Two barriers: the result words are next written by wave 0 after
+        // the following level's first barrier, which every wave reaches only
+        // once it has read them.
+        if (threadIdx.x < (unsigned)kWave) {
+            // One bin at a time: the caller's keys are live in registers here.
+#pragma unroll 1
+            for (int q = 0; q < 4; ++q) {
+                const int b = lane + q * kWave;
+                uint32_t t = 0;
 #pragma unroll
-        for (int c = 0; c < kLevelCopies; ++c) {
-            t += sm.hist[c][b];
-            sm.hist[c][b] = 0u;  // clear for the next level
+                for (int c = 0; c < kLevelCopies; ++c) {
+                    t += sm.hist[c][b];
+                    sm.hist[c][b] = 0u;
+                }
+                sm.bins[b] = t;
+            }
+            wave_lds_sync();
         }
-        sm.bins[b] = t;
+    } else {
+        for (int b = threadIdx.x; b < 256; b += blockDim.x) {  // the block may have < 256 threads
+            uint32_t t = 0;
+#pragma unroll
+            for (int c = 0; c < kLevelCopies; ++c) {
+                t += sm.hist[c][b];
+                sm.hist[c][b] = 0u;
+            }
+            sm.bins[b] = t;
+        }
+        lds_barrier();
     }
-    lds_barrier();
-    if (wave == 0) {
+    if (threadIdx.x < (unsigned)kWave) {
         int nd = need;
         uint32_t b, c;
         const bool ok = radix_find(sm.bins, nd, b, c);
@@ -72,7 +102,7 @@ __device__ __forceinline__ bool level_hist_find(Smem& sm, int& need, uint32_t& b
     bin = sm.bc[1];
     cb = sm.bc[2];
     if (ok) need = (int)sm.bc[3];
-    lds_barrier();  // sm.bc is rewritten by the next level
+    if constexpr (!Wave0Find<Smem>::value) lds_barrier();  // sm.bc is rewritten by the next level
     return ok;
 }
 

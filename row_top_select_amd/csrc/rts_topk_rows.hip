@@ -633,6 +633,7 @@ void topk_rows_stream_kernel(
 // ---------------------------------------------------------------------------
 template <int NW>
 struct BlockRowSmem {
+    static constexpr bool kWave0Find = true;
     uint32_t hist[kLevelCopies][kLevelStride];
     uint32_t bins[256];
     uint32_t bc[4];
@@ -655,7 +656,11 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
     static_assert(KPT % 4 == 0, "keys come in groups of four");
     __shared__ BlockRowSmem<NW> sm;
     constexpr int CAPL = 128;     // boundary-bin list entries per wave
+    // A second sort exchange buffer for 8 waves (six cross-wave steps); with
+    // 4 waves the LDS would cost workgroups per CU.
+    constexpr bool kSortDoubleBuffer = NW >= 8;
     __shared__ uint64_t buf[LS];
+    __shared__ uint64_t buf2[kSortDoubleBuffer ? LS : 1];
     __shared__ uint64_t lst[NW][CAPL];
     const int t = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
@@ -937,20 +942,26 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
 #pragma unroll
     for (int r = 0; r < E; ++r) v[r] = buf[wave * S + lane * E + r];
     wave_bitonic_sort_dir<E>(v, (wave & 1) == 0);
+    // Cross-wave steps exchange through LDS.  With two exchange buffers
+    // used in turn, a step's write cannot meet the previous step's reads
+    // (those end before that step's barrier), so a step takes one barrier.
+    int xi = 0;
 #pragma unroll
     for (int K = 2 * S; K <= LS; K *= 2) {
         const bool desc = ((wave * S) & K) == 0;
 #pragma unroll
         for (int J = K / 2; J >= S; J /= 2) {
-            lds_barrier();
+            uint64_t* xb = (kSortDoubleBuffer && (xi & 1)) ? buf2 : buf;
+            ++xi;
+            if (!kSortDoubleBuffer) lds_barrier();
 #pragma unroll
-            for (int r = 0; r < E; ++r) buf[wave * S + lane * E + r] = v[r];
+            for (int r = 0; r < E; ++r) xb[wave * S + lane * E + r] = v[r];
             lds_barrier();
             const int pw = wave ^ (J / S);
             const bool keep_max = (wave < pw) == desc;
 #pragma unroll
             for (int r = 0; r < E; ++r) {
-                const uint64_t o = buf[pw * S + lane * E + r];
+                const uint64_t o = xb[pw * S + lane * E + r];
                 v[r] = keep_max ? umax64(v[r], o) : umin64(v[r], o);
             }
         }
