@@ -697,7 +697,19 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T*>(rowp), (short)0, ei * (int)sizeof(T), 0x00020000);
     const bool vec_ok = (reinterpret_cast<uintptr_t>(rowp) % sizeof(V)) == 0;
-    uint32_t key[KPT];
+    // The row as fp32 bits (bf16 widened), every empty slot (past the row
+    // end, or NaN) the quiet NaN kEmpty: ordered compares on it are false,
+    // and a key is formed only where one is needed.
+    constexpr uint32_t kEmpty = 0x7FC00000u;
+    uint32_t fb[KPT];
+    // The passes that need every key (the register levels, the selection
+    // below) turn fb into keys in place first (0 for an empty slot).
+    bool keyed = false;
+    auto to_keys = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) fb[i] = fb[i] == kEmpty ? 0u : key32_of_bits(fb[i]);
+        keyed = true;
+    };
     {
         V raw[KPT / 4];
         const int voff = t * (int)sizeof(V);
@@ -724,24 +736,36 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
                         bits[j] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (c0 + j) * 4, 0, 0);
                 }
             }
+            if ((g + 1) * NT * 4 <= ei) {  // the whole group is inside the row end, for every lane
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bool ok = c0 + j < ei && !f32_bits_is_nan(bits[j]);
-                key[4 * g + j] = ok ? key32_of_bits(bits[j]) : 0u;
+                for (int j = 0; j < 4; ++j)
+                    fb[4 * g + j] = __builtin_isnan(__uint_as_float(bits[j])) ? kEmpty : bits[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = c0 + j < ei && !__builtin_isnan(__uint_as_float(bits[j]));
+                    fb[4 * g + j] = ok ? bits[j] : kEmpty;
+                }
             }
         }
     }
 
-    // Valid count and key range (every valid key is >= key32(-inf) > 0; the
-    // minimum is taken over key - 1, which sends empty slots to the top).
-    // Per-lane figures, then the wave's, then lane w < NW combines wave w's.
-    uint32_t nv = 0, mn = 0xFFFFFFFFu, mx = 0u;
+    // Valid count and key range: per lane in floats (compare and select,
+    // which passes over kEmpty), then as keys for the wave and workgroup
+    // reductions (lane w < NW combines wave w's).  A lane's zero minimum
+    // (maximum) counts as -0 (+0): a compare does not order the two zeros.
+    uint32_t nv = 0, mn, mx;
+    {
+        float fmn = __builtin_inff(), fmx = -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        nv += key[i] != 0u ? 1u : 0u;
-        const uint32_t km1 = key[i] - 1u;
-        mn = km1 < mn ? km1 : mn;
-        mx = key[i] > mx ? key[i] : mx;
+        for (int i = 0; i < KPT; ++i) {
+            const float f = __uint_as_float(fb[i]);
+            nv += __builtin_isnan(f) ? 0u : 1u;
+            fmn = f < fmn ? f : fmn;
+            fmx = f > fmx ? f : fmx;
+        }
+        mn = fmn == 0.0f ? 0x7FFFFFFFu : key32_of_bits(__float_as_uint(fmn));  // key of -0
+        mx = fmx == 0.0f ? 0x80000000u : key32_of_bits(__float_as_uint(fmx));  // key of +0
     }
     nv = wave_sum32(nv);
     mn = wave_min32(mn);
@@ -758,7 +782,6 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
         mn = wave_min32(wl ? sm.red[lane][1] : 0xFFFFFFFFu);
         mx = wave_max32(wl ? sm.red[lane][2] : 0u);
     }
-    mn += 1u;
 
     // Selected: key > thr_gt, or key == tie_key and column <= col_cut.
     uint32_t thr_gt = 0u, tie_key = 0u, col_cut = 0u;
@@ -770,7 +793,7 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
         auto visit = [&](auto f) __attribute__((always_inline)) {
             const uint32_t cb = col_base();
 #pragma unroll
-            for (int i = 0; i < KPT; ++i) f(key[i], col_at(cb, i));
+            for (int i = 0; i < KPT; ++i) f(fb[i], col_at(cb, i));  // fb holds keys here
         };
         int need = k;
         uint32_t wlo = mn, whi = mx;
@@ -784,15 +807,17 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
         const float lo = float_of_key32(mn), hi = float_of_key32(mx);
         const float scale = 256.0f / (hi - lo);
         if (__builtin_isfinite(lo) && __builtin_isfinite(hi) && hi > lo && __builtin_isfinite(scale)) {
-            auto vbin = [&](uint32_t kk) -> uint32_t {
-                const float tb = (float_of_key32(kk) - lo) * scale;  // in [0, 256]
-                return (uint32_t)(tb < 255.0f ? tb : 255.0f);
-            };
-            // Empty slots count into the padding word 256, which no level reads.
+            // tb = (v - lo) * scale lies in [0, 256] for a value, NaN for an
+            // empty slot, which counts into the padding word 256 (no level
+            // reads it).
 #pragma unroll
-            for (int i = 0; i < KPT; ++i)
-                __hip_atomic_fetch_add(&sm.hist[lane & (kLevelCopies - 1)][key[i] != 0u ? vbin(key[i]) : 256u],
-                                       1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            for (int i = 0; i < KPT; ++i) {
+                const float tb = (__uint_as_float(fb[i]) - lo) * scale;
+                const uint32_t tbi = (uint32_t)tb;
+                const uint32_t vb = tb >= 0.0f ? (tbi < 255u ? tbi : 255u) : 256u;
+                __hip_atomic_fetch_add(&sm.hist[lane & (kLevelCopies - 1)][vb], 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
             uint32_t bin, cbin;
             if (level_hist_find(sm, need, bin, cbin)) {
                 // One pass over the keys: a key in a bin above the boundary bin
@@ -809,20 +834,24 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
                 // (a register per key).
                 float lo2 = lo;
                 asm volatile("" : "+v"(lo2));
+                // The bin test as compares on tb: bin(v) > bin iff tb >= bin + 1
+                // (never for the top bin), bin(v) == bin iff bin <= tb and not
+                // above; both are false for an empty slot.
+                const float t_in = (float)bin;
+                const float t_above = bin < 255u ? (float)(bin + 1u) : __builtin_inff();
 #pragma unroll
                 for (int i = 0; i < KPT; ++i) {
-                    const float tb = (float_of_key32(key[i]) - lo2) * scale;
-                    const uint32_t vb = (uint32_t)(tb < 255.0f ? tb : 255.0f);
-                    const bool ok = key[i] != 0u;
-                    const bool above = ok && vb > bin;
+                    const float tb = (__uint_as_float(fb[i]) - lo2) * scale;
+                    const bool above = tb >= t_above;
                     amask |= above ? (1u << i) : 0u;
                     na += above ? 1u : 0u;
-                    if (ok && vb == bin) {
+                    if (tb >= t_in && !above) {
+                        const uint32_t kk = key32_of_bits(fb[i]);
                         const uint32_t pos = __hip_atomic_fetch_add(&sm.nlist[wave], 1u, __ATOMIC_RELAXED,
                                                                     __HIP_MEMORY_SCOPE_WORKGROUP);
-                        if (pos < (uint32_t)CAPL) lst[wave][pos] = composite(key[i], col_at(cbl, i));
-                        lmn = key[i] < lmn ? key[i] : lmn;
-                        lmx = key[i] > lmx ? key[i] : lmx;
+                        if (pos < (uint32_t)CAPL) lst[wave][pos] = composite(kk, col_at(cbl, i));
+                        lmn = kk < lmn ? kk : lmn;
+                        lmx = kk > lmx ? kk : lmx;
                     }
                 }
                 const uint32_t na_incl = wave_incl_scan32(na);
@@ -876,7 +905,7 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
 #pragma unroll
                     for (int i = 0; i < KPT; ++i) {
                         const uint32_t a = (amask >> i) & 1u;
-                        if (a) buf[q] = composite(key[i], col_at(cbw, i));
+                        if (a) buf[q] = composite(key32_of_bits(fb[i]), col_at(cbw, i));
                         q += a;
                     }
                     for (uint32_t p = (uint32_t)lane; p < nl; p += kWave) {
@@ -902,6 +931,7 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
             }
         }
         if (!done) {
+            to_keys();
             const uint32_t span = whi - wlo;
             const int bl = span ? 32 - __clz((int)span) : 0;
             const uint32_t sh = bl > 8 ? (uint32_t)(bl - 8) : 0u;
@@ -914,10 +944,11 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
 
     if (!written) {
         // The selected composites into LDS (any order), empty slots after them.
+        if (!keyed) to_keys();
         uint32_t cnt = 0;
         uint32_t cb = col_base();
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) cnt += (uint32_t)__popcll(__ballot(selected(key[i], col_at(cb, i))));
+        for (int i = 0; i < KPT; ++i) cnt += (uint32_t)__popcll(__ballot(selected(fb[i], col_at(cb, i))));
         if (lane == 0) sm.red[wave][3] = cnt;
         lds_barrier();
         const uint32_t incl = wave_incl_scan32(lane < NW ? sm.red[lane][3] : 0u);
@@ -927,10 +958,11 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const uint32_t c = col_at(cb, i);
-            const bool sel = selected(key[i], c);
+            const uint32_t kk = fb[i];
+            const bool sel = selected(kk, c);
             const uint64_t m = __ballot(sel);
             const uint32_t pos = off + mbcnt64(m);
-            if (sel && pos < (uint32_t)LS) buf[pos] = composite(key[i], c);
+            if (sel && pos < (uint32_t)LS) buf[pos] = composite(kk, c);
             off += (uint32_t)__popcll(m);
         }
         for (int p = (int)(total < (uint32_t)LS ? total : (uint32_t)LS) + t; p < LS; p += NT) buf[p] = 0ull;
