@@ -881,21 +881,28 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
                 }
                 if ((int)cbin == need) thr_gt = bmn - 1u;  // the whole bin is taken: keys >= its smallest
                 if (fits) {
+                    // The list's levels on the keys' significant bits: a bf16
+                    // key varies only in its top 16 (the rest follow the sign),
+                    // so ties show at the first level there.  lthr / ltie /
+                    // lcut: the selection rule in those units.
+                    constexpr int KS = BF16 ? 16 : 0;
+                    uint32_t lthr = (bmn >> KS) - 1u, ltie = 0u, lcut = 0u;  // whole bin taken
                     if ((int)cbin != need) {
                         const uint32_t mine = nl;  // this wave's list entries
                         auto visit_list = [&](auto f) __attribute__((always_inline)) {
                             for (uint32_t p = (uint32_t)lane; p < mine; p += kWave) {
                                 const uint64_t c = lst[wave][p];
-                                f((uint32_t)(c >> 32), composite_id(c));
+                                f((uint32_t)(c >> (32 + KS)), composite_id(c));
                             }
                         };
-                        const uint32_t span = bmx - bmn;
+                        const uint32_t llo = bmn >> KS, lhi = bmx >> KS;
+                        const uint32_t span = lhi - llo;
                         const int bl = span ? 32 - __clz((int)span) : 0;
                         const uint32_t sh = bl > 8 ? (uint32_t)(bl - 8) : 0u;
                         bool ties;
                         uint32_t ntie;
-                        radix_levels(sm, visit_list, need, bmn, span, sh, bmx, thr_gt, ties, tie_key, ntie);
-                        if (ties) col_cut = tie_cut(sm, visit_list, tie_key, ntie, need, (uint32_t)(cols - 1));
+                        radix_levels(sm, visit_list, need, llo, span, sh, lhi, lthr, ties, ltie, ntie);
+                        if (ties) lcut = tie_cut(sm, visit_list, ltie, ntie, need, (uint32_t)(cols - 1));
                     }
                     // The selected: keys above the boundary bin at this wave's
                     // offset, then the list's selected after all of those (any
@@ -910,7 +917,8 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
                     }
                     for (uint32_t p = (uint32_t)lane; p < nl; p += kWave) {
                         const uint64_t c = lst[wave][p];
-                        if (selected((uint32_t)(c >> 32), composite_id(c))) {
+                        const uint32_t kk = (uint32_t)(c >> (32 + KS));
+                        if (kk > lthr || (kk == ltie && composite_id(c) <= lcut)) {
                             const uint32_t q = __hip_atomic_fetch_add(&sm.nsel, 1u, __ATOMIC_RELAXED,
                                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
                             buf[atot + q] = c;
