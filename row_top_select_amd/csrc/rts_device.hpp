@@ -137,8 +137,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // elements l*N .. l*N+N-1 in v[0..N-1].  Partners closer than N are in the
 // same lane; farther partners are exchanged with a lane xor.  Which lanes sort
 // a pair descending, or keep the larger partner, is a fixed pattern of lane
-// bits per stage, so a compare-exchange is one 64-bit compare, one scalar xor
-// of wave masks and a select per word.
+// bits per stage, so a compare-exchange is one compare, one scalar xor of
+// wave masks and a select per word.  Elements are 32-bit keys or 64-bit
+// composites (uint32_t or uint64_t arrays).
 // ---------------------------------------------------------------------------
 
 // Lanes whose index has bit x set (x a power of two); none for x >= 64.
@@ -158,10 +159,21 @@ __device__ __forceinline__ uint64_t select64_by_mask(uint64_t m, uint64_t if_set
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Lane exchange and select for either element width of the networks below
+// (32-bit keys, or 64-bit composites).
+__device__ __forceinline__ uint32_t lane_xor_k(uint32_t v, int lj) { return lane_xor32(v, lj); }
+__device__ __forceinline__ uint64_t lane_xor_k(uint64_t v, int lj) { return shfl_xor64(v, lj); }
+__device__ __forceinline__ uint32_t select_k(uint64_t m, uint32_t if_set, uint32_t if_clear) {
+    return select_by_mask(m, if_set, if_clear);
+}
+__device__ __forceinline__ uint64_t select_k(uint64_t m, uint64_t if_set, uint64_t if_clear) {
+    return select64_by_mask(m, if_set, if_clear);
+}
+
 // flip = ~0: the whole network sorts descending (a wave-uniform value, so
 // the direction may also be chosen at run time).
-template <int N, int K, int J>
-__device__ __forceinline__ void bitonic_stage_flip(uint64_t (&v)[N], uint64_t flip) {
+template <int N, int K, int J, typename U>
+__device__ __forceinline__ void bitonic_stage_flip(U (&v)[N], uint64_t flip) {
     // Element i = l*N + r lies in an ascending run iff (i & K) == 0 (the
     // reverse when flipped).  For K >= N that is bit K/N of the lane.
     if constexpr (J < N) {
@@ -170,11 +182,11 @@ __device__ __forceinline__ void bitonic_stage_flip(uint64_t (&v)[N], uint64_t fl
             if ((r & J) == 0) {
                 const uint64_t desc =
                     (K < N ? (((r & K) != 0) ? ~0ull : 0ull) : lanes_with_bit(K / N)) ^ flip;
-                const uint64_t a = v[r], b = v[r | J];
+                const U a = v[r], b = v[r | J];
                 // Ascending: swap if a > b; descending: if a < b (equal: either).
                 const uint64_t sw = __ballot(a > b) ^ desc;
-                v[r] = select64_by_mask(sw, b, a);
-                v[r | J] = select64_by_mask(sw, a, b);
+                v[r] = select_k(sw, b, a);
+                v[r | J] = select_k(sw, a, b);
             }
         }
     } else {
@@ -184,24 +196,24 @@ __device__ __forceinline__ void bitonic_stage_flip(uint64_t (&v)[N], uint64_t fl
         const uint64_t keep_max = lanes_with_bit(LJ) ^ desc;
 #pragma unroll
         for (int r = 0; r < N; ++r) {
-            const uint64_t o = shfl_xor64(v[r], LJ);
+            const U o = lane_xor_k(v[r], LJ);
             const uint64_t take = __ballot(v[r] > o) ^ keep_max;
-            v[r] = select64_by_mask(take, o, v[r]);
+            v[r] = select_k(take, o, v[r]);
         }
     }
 }
 
 // Stages J, J/2, .., 1 of the merge step of size K.
-template <int N, int K, int J>
-__device__ __forceinline__ void bitonic_steps(uint64_t (&v)[N], uint64_t flip) {
+template <int N, int K, int J, typename U>
+__device__ __forceinline__ void bitonic_steps(U (&v)[N], uint64_t flip) {
     if constexpr (J >= 1) {
         bitonic_stage_flip<N, K, J>(v, flip);
         bitonic_steps<N, K, J / 2>(v, flip);
     }
 }
 
-template <int N, int K>
-__device__ __forceinline__ void bitonic_sort_from(uint64_t (&v)[N], uint64_t flip) {
+template <int N, int K, typename U>
+__device__ __forceinline__ void bitonic_sort_from(U (&v)[N], uint64_t flip) {
     if constexpr (K <= kWave * N) {
         bitonic_steps<N, K, K / 2>(v, flip);
         bitonic_sort_from<N, K * 2>(v, flip);
@@ -210,15 +222,15 @@ __device__ __forceinline__ void bitonic_sort_from(uint64_t (&v)[N], uint64_t fli
 
 // Full sort: ascending (DESC=false) or descending.  Every stage is its own
 // instantiation, so k and j are constants without relying on loop unrolling.
-template <int N, bool DESC>
-__device__ __forceinline__ void wave_bitonic_sort(uint64_t (&v)[N]) {
+template <int N, bool DESC, typename U>
+__device__ __forceinline__ void wave_bitonic_sort(U (&v)[N]) {
     bitonic_sort_from<N, 2>(v, DESC ? ~0ull : 0ull);
 }
 
 // Sorts a bitonic sequence (e.g. the elementwise max of a descending and an
 // ascending sorted sequence).
-template <int N, bool DESC>
-__device__ __forceinline__ void wave_bitonic_merge(uint64_t (&v)[N]) {
+template <int N, bool DESC, typename U>
+__device__ __forceinline__ void wave_bitonic_merge(U (&v)[N]) {
     bitonic_steps<N, kWave * N, kWave * N / 2>(v, DESC ? ~0ull : 0ull);
 }
 
@@ -228,12 +240,12 @@ __device__ __forceinline__ uint64_t uniform_flip(bool desc) {
     const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane(desc ? -1 : 0);
     return ((uint64_t)f << 32) | f;
 }
-template <int N>
-__device__ __forceinline__ void wave_bitonic_sort_dir(uint64_t (&v)[N], bool desc) {
+template <int N, typename U>
+__device__ __forceinline__ void wave_bitonic_sort_dir(U (&v)[N], bool desc) {
     bitonic_sort_from<N, 2>(v, uniform_flip(desc));
 }
-template <int N>
-__device__ __forceinline__ void wave_bitonic_merge_dir(uint64_t (&v)[N], bool desc) {
+template <int N, typename U>
+__device__ __forceinline__ void wave_bitonic_merge_dir(U (&v)[N], bool desc) {
     bitonic_steps<N, kWave * N, kWave * N / 2>(v, uniform_flip(desc));
 }
 

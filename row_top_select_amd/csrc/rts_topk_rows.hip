@@ -31,6 +31,7 @@
 // The result is exact for any distribution; adversarial orders only cost more
 // compactions, never more HBM traffic.
 #include <mutex>
+#include <type_traits>
 
 #include "rts_device.hpp"
 #include "rts_internal.h"
@@ -659,8 +660,19 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
     // A second sort exchange buffer for 8 waves (six cross-wave steps); with
     // 4 waves the LDS would cost workgroups per CU.
     constexpr bool kSortDoubleBuffer = NW >= 8;
-    __shared__ uint64_t buf[LS];
-    __shared__ uint64_t buf2[kSortDoubleBuffer ? LS : 1];
+    // Sort elements: for bf16 one 32-bit word, the key's top 16 bits (the
+    // rest follow the sign) over 0xFFFF - column (columns < 2^14 here), with
+    // the order of the 64-bit composite; for fp32 the composite.  0: empty.
+    using SK = std::conditional_t<BF16, uint32_t, uint64_t>;
+    auto sort_key = [](uint32_t key, uint32_t col) -> SK {
+        if constexpr (BF16)
+            return (key & 0xFFFF0000u) | (0xFFFFu - col);
+        else
+            return composite(key, col);
+    };
+    auto sort_key_of = [&](uint64_t c) -> SK { return sort_key((uint32_t)(c >> 32), composite_id(c)); };
+    __shared__ SK buf[LS];
+    __shared__ SK buf2[kSortDoubleBuffer ? LS : 1];
     __shared__ uint64_t lst[NW][CAPL];
     const int t = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
@@ -912,7 +924,7 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
 #pragma unroll
                     for (int i = 0; i < KPT; ++i) {
                         const uint32_t a = (amask >> i) & 1u;
-                        if (a) buf[q] = composite(key32_of_bits(fb[i]), col_at(cbw, i));
+                        if (a) buf[q] = sort_key(key32_of_bits(fb[i]), col_at(cbw, i));
                         q += a;
                     }
                     for (uint32_t p = (uint32_t)lane; p < nl; p += kWave) {
@@ -921,10 +933,10 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
                         if (kk > lthr || (kk == ltie && composite_id(c) <= lcut)) {
                             const uint32_t q = __hip_atomic_fetch_add(&sm.nsel, 1u, __ATOMIC_RELAXED,
                                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-                            buf[atot + q] = c;
+                            buf[atot + q] = sort_key_of(c);
                         }
                     }
-                    for (int p = k + t; p < LS; p += NT) buf[p] = 0ull;
+                    for (int p = k + t; p < LS; p += NT) buf[p] = 0;
                     written = true;
                     done = true;
                 } else {
@@ -970,15 +982,15 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
             const bool sel = selected(kk, c);
             const uint64_t m = __ballot(sel);
             const uint32_t pos = off + mbcnt64(m);
-            if (sel && pos < (uint32_t)LS) buf[pos] = composite(kk, c);
+            if (sel && pos < (uint32_t)LS) buf[pos] = sort_key(kk, c);
             off += (uint32_t)__popcll(m);
         }
-        for (int p = (int)(total < (uint32_t)LS ? total : (uint32_t)LS) + t; p < LS; p += NT) buf[p] = 0ull;
+        for (int p = (int)(total < (uint32_t)LS ? total : (uint32_t)LS) + t; p < LS; p += NT) buf[p] = 0;
     }
     lds_barrier();
 
     // Descending sort of the LS slots; element i = wave * S + lane * E + r.
-    uint64_t v[E];
+    SK v[E];
 #pragma unroll
     for (int r = 0; r < E; ++r) v[r] = buf[wave * S + lane * E + r];
     wave_bitonic_sort_dir<E>(v, (wave & 1) == 0);
@@ -991,7 +1003,7 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
         const bool desc = ((wave * S) & K) == 0;
 #pragma unroll
         for (int J = K / 2; J >= S; J /= 2) {
-            uint64_t* xb = (kSortDoubleBuffer && (xi & 1)) ? buf2 : buf;
+            SK* xb = (kSortDoubleBuffer && (xi & 1)) ? buf2 : buf;
             ++xi;
             if (!kSortDoubleBuffer) lds_barrier();
 #pragma unroll
@@ -1001,8 +1013,8 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
             const bool keep_max = (wave < pw) == desc;
 #pragma unroll
             for (int r = 0; r < E; ++r) {
-                const uint64_t o = xb[pw * S + lane * E + r];
-                v[r] = keep_max ? umax64(v[r], o) : umin64(v[r], o);
+                const SK o = xb[pw * S + lane * E + r];
+                v[r] = keep_max ? (v[r] < o ? o : v[r]) : (v[r] < o ? v[r] : o);
             }
         }
         wave_bitonic_merge_dir<E>(v, desc);
@@ -1011,7 +1023,12 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
 #pragma unroll
     for (int r = 0; r < E; ++r) {
         const int i = wave * S + lane * E + r;
-        if (i < k) o_row[i] = v[r] ? (int32_t)composite_id(v[r]) : -1;
+        if (i < k) {
+            if constexpr (BF16)
+                o_row[i] = v[r] ? (int32_t)(0xFFFFu - (v[r] & 0xFFFFu)) : -1;
+            else
+                o_row[i] = v[r] ? (int32_t)composite_id(v[r]) : -1;
+        }
     }
 }
 
