@@ -657,9 +657,10 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
     static_assert(KPT % 4 == 0, "keys come in groups of four");
     __shared__ BlockRowSmem<NW> sm;
     constexpr int CAPL = 128;     // boundary-bin list entries per wave
-    // A second sort exchange buffer for 8 waves (six cross-wave steps); with
-    // 4 waves the LDS would cost workgroups per CU.
-    constexpr bool kSortDoubleBuffer = NW >= 8;
+    // A second sort exchange buffer for 8 waves (six cross-wave steps) of
+    // 32-bit elements; with 64-bit ones, or 4 waves, the LDS would cost
+    // workgroups per CU.
+    constexpr bool kSortDoubleBuffer = NW >= 8 && BF16;
     // Sort elements: for bf16 one 32-bit word, the key's top 16 bits (the
     // rest follow the sign) over 0xFFFF - column (columns < 2^14 here), with
     // the order of the 64-bit composite; for fp32 the composite.  0: empty.
@@ -982,7 +983,14 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
             const bool sel = selected(kk, c);
             const uint64_t m = __ballot(sel);
             const uint32_t pos = off + mbcnt64(m);
-            if (sel && pos < (uint32_t)LS) buf[pos] = sort_key(kk, c);
+            if (sel && pos < (uint32_t)LS) {
+                // The key through a copy in another register: a composite
+                // built on the register itself would pin every key to the odd
+                // half of an aligned register pair.
+                uint32_t kc;
+                asm volatile("v_mov_b32 %0, %1" : "=&v"(kc) : "v"(kk));
+                buf[pos] = sort_key(kc, c);
+            }
             off += (uint32_t)__popcll(m);
         }
         for (int p = (int)(total < (uint32_t)LS ? total : (uint32_t)LS) + t; p < LS; p += NT) buf[p] = 0;
