@@ -997,45 +997,146 @@ __global__ __launch_bounds__(kWave* NW) void topk_rows_block_kernel(
     }
     lds_barrier();
 
-    // Descending sort of the LS slots; element i = wave * S + lane * E + r.
-    SK v[E];
-#pragma unroll
-    for (int r = 0; r < E; ++r) v[r] = buf[wave * S + lane * E + r];
-    wave_bitonic_sort_dir<E>(v, (wave & 1) == 0);
-    // Cross-wave steps exchange through LDS.  With two exchange buffers
-    // used in turn, a step's write cannot meet the previous step's reads
-    // (those end before that step's barrier), so a step takes one barrier.
-    int xi = 0;
-#pragma unroll
-    for (int K = 2 * S; K <= LS; K *= 2) {
-        const bool desc = ((wave * S) & K) == 0;
-#pragma unroll
-        for (int J = K / 2; J >= S; J /= 2) {
-            SK* xb = (kSortDoubleBuffer && (xi & 1)) ? buf2 : buf;
-            ++xi;
-            if (!kSortDoubleBuffer) lds_barrier();
-#pragma unroll
-            for (int r = 0; r < E; ++r) xb[wave * S + lane * E + r] = v[r];
-            lds_barrier();
-            const int pw = wave ^ (J / S);
-            const bool keep_max = (wave < pw) == desc;
+    // fp32 rows with the k selected in buf: each goes straight to its place,
+    // no sort network.  Buckets of the selected keys' range from the top
+    // (2^bits of them, bits from the LDS the list used) order the keys
+    // between buckets; a key's place in its bucket is the count of its
+    // bucket-mates with a larger composite.  Buckets of more than 32 (ties,
+    // crowded values) leave the row to the network below.
+    bool ranked = false;
+    if constexpr (!BF16) {
+        if (written) {
+            constexpr int NB = NW * CAPL * 2;  // buckets: the list's LDS as words
+            constexpr int BPT = NB / NT;       // buckets per thread (4)
+            static_assert(BPT * NT == NB && NB <= 65536, "bucket layout");
+            constexpr int NBB = NB == 2048 ? 11 : NB == 1024 ? 10 : 12;
+            static_assert((1 << NBB) == NB, "buckets are a power of two");
+            uint32_t* bcount = reinterpret_cast<uint32_t*>(&lst[0][0]);
+            uint16_t* bidx = reinterpret_cast<uint16_t*>(&sm.hist[0][0]);
+            static_assert(sizeof(sm.hist) >= LS * sizeof(uint16_t), "index list fits the histogram");
+            SK v[E];
+            uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
             for (int r = 0; r < E; ++r) {
-                const SK o = xb[pw * S + lane * E + r];
-                v[r] = keep_max ? (v[r] < o ? o : v[r]) : (v[r] < o ? v[r] : o);
+                v[r] = buf[t * E + r];
+                const uint32_t kk = (uint32_t)(v[r] >> 32);
+                if (t * E + r < k) {
+                    kmn = kk < kmn ? kk : kmn;
+                    kmx = kk > kmx ? kk : kmx;
+                }
+            }
+            kmn = wave_min32(kmn);
+            kmx = wave_max32(kmx);
+            if (lane == 0) {
+                sm.red[wave][0] = kmn;
+                sm.red[wave][1] = kmx;
+            }
+            for (int q = t; q < NB; q += NT) bcount[q] = 0u;
+            lds_barrier();
+            kmn = wave_min32(lane < NW ? sm.red[lane][0] : 0xFFFFFFFFu);
+            kmx = wave_max32(lane < NW ? sm.red[lane][1] : 0u);
+            const uint32_t span = kmx - kmn;
+            const int sbits = span ? 32 - __clz((int)span) : 0;
+            const uint32_t bsh = sbits > NBB ? (uint32_t)(sbits - NBB) : 0u;
+            uint32_t bk[E], slot[E];
+#pragma unroll
+            for (int r = 0; r < E; ++r) {
+                bk[r] = (kmx - (uint32_t)(v[r] >> 32)) >> bsh;  // < NB
+                slot[r] = 0u;
+                if (t * E + r < k)
+                    slot[r] = __hip_atomic_fetch_add(&bcount[bk[r]], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            lds_barrier();
+            // Bucket starts: this thread's BPT buckets, a wave scan, the waves' totals.
+            uint32_t c[BPT], tot = 0u, cmax = 0u;
+#pragma unroll
+            for (int j = 0; j < BPT; ++j) {
+                c[j] = bcount[t * BPT + j];
+                tot += c[j];
+                cmax = c[j] > cmax ? c[j] : cmax;
+            }
+            const uint32_t incl = wave_incl_scan32(tot);
+            cmax = wave_max32(cmax);
+            if (lane == 0) {
+                sm.red[wave][2] = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+                sm.red[wave][3] = cmax;
+            }
+            lds_barrier();
+            const uint32_t wincl = wave_incl_scan32(lane < NW ? sm.red[lane][2] : 0u);
+            const uint32_t woff = wave == 0 ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)wincl, wave - 1);
+            const uint32_t big = wave_max32(lane < NW ? sm.red[lane][3] : 0u);
+            if (big <= 32u) {
+                uint32_t st = woff + incl - tot;
+#pragma unroll
+                for (int j = 0; j < BPT; ++j) {
+                    bcount[t * BPT + j] = st;  // each thread rewrites only its own buckets
+                    st += c[j];
+                }
+                lds_barrier();
+                uint32_t bst[E], ben[E];
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    bst[r] = bcount[bk[r]];
+                    ben[r] = bk[r] + 1 < (uint32_t)NB ? bcount[bk[r] + 1] : (uint32_t)k;
+                    if (t * E + r < k) bidx[bst[r] + slot[r]] = (uint16_t)(t * E + r);
+                }
+                lds_barrier();
+                int32_t* o_row = out + row * ld_out;
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    if (t * E + r < k) {
+                        uint32_t above = 0u;
+                        for (uint32_t q = bst[r]; q < ben[r]; ++q) above += buf[bidx[q]] > v[r] ? 1u : 0u;
+                        o_row[bst[r] + above] = (int32_t)composite_id(v[r]);
+                    }
+                }
+                ranked = true;
             }
         }
-        wave_bitonic_merge_dir<E>(v, desc);
     }
-    int32_t* o_row = out + row * ld_out;
-#pragma unroll
-    for (int r = 0; r < E; ++r) {
-        const int i = wave * S + lane * E + r;
-        if (i < k) {
-            if constexpr (BF16)
-                o_row[i] = v[r] ? (int32_t)(0xFFFFu - (v[r] & 0xFFFFu)) : -1;
-            else
-                o_row[i] = v[r] ? (int32_t)composite_id(v[r]) : -1;
+
+    if (!ranked) {
+        // Descending sort of the LS slots; element i = wave * S + lane * E + r.
+        SK v[E];
+    #pragma unroll
+        for (int r = 0; r < E; ++r) v[r] = buf[wave * S + lane * E + r];
+        wave_bitonic_sort_dir<E>(v, (wave & 1) == 0);
+        // Cross-wave steps exchange through LDS.  With two exchange buffers
+        // used in turn, a step's write cannot meet the previous step's reads
+        // (those end before that step's barrier), so a step takes one barrier.
+        int xi = 0;
+    #pragma unroll
+        for (int K = 2 * S; K <= LS; K *= 2) {
+            const bool desc = ((wave * S) & K) == 0;
+    #pragma unroll
+            for (int J = K / 2; J >= S; J /= 2) {
+                SK* xb = (kSortDoubleBuffer && (xi & 1)) ? buf2 : buf;
+                ++xi;
+                if (!kSortDoubleBuffer) lds_barrier();
+    #pragma unroll
+                for (int r = 0; r < E; ++r) xb[wave * S + lane * E + r] = v[r];
+                lds_barrier();
+                const int pw = wave ^ (J / S);
+                const bool keep_max = (wave < pw) == desc;
+    #pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    const SK o = xb[pw * S + lane * E + r];
+                    v[r] = keep_max ? (v[r] < o ? o : v[r]) : (v[r] < o ? v[r] : o);
+                }
+            }
+            wave_bitonic_merge_dir<E>(v, desc);
+        }
+        int32_t* o_row = out + row * ld_out;
+    #pragma unroll
+        for (int r = 0; r < E; ++r) {
+            const int i = wave * S + lane * E + r;
+            if (i < k) {
+                if constexpr (BF16)
+                    o_row[i] = v[r] ? (int32_t)(0xFFFFu - (v[r] & 0xFFFFu)) : -1;
+                else
+                    o_row[i] = v[r] ? (int32_t)composite_id(v[r]) : -1;
+            }
         }
     }
 }
