@@ -34,7 +34,8 @@ PEAK_HBM_GBS = 8000.0                  # MI355X HBM3E
 PAGES_ROWS_PER_S = 4096 / 499.9e-6     # best published rate on this workload (GB200, context)
 COUNTERS = os.path.join(ROOT, "profiles", "topk_rows_verylong_counters.json")
 KERNEL_SOURCES = ["row_top_select_amd/csrc/rts_topk_rows.hip",
-                  "row_top_select_amd/csrc/rts_device.hpp"]
+                  "row_top_select_amd/csrc/rts_device.hpp",
+                  "row_top_select_amd/csrc/rts_levels.hpp"]
 
 
 def log(*a):
