@@ -261,12 +261,20 @@ def test_block_rows_random(rts, dtype, cols, k):
         check(rts, x, ends, k, what=f"block {cols} {k}")
 
 
-@pytest.mark.parametrize("case", ["ties", "specials", "equal", "ascending", "plus100"])
-def test_block_rows_adversarial(rts, case):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", ["ties", "specials", "equal", "ascending", "plus100", "dup"])
+def test_block_rows_adversarial(rts, case, dtype):
     rng = np.random.default_rng(17)
     rows, cols, k = 260, 16384, 2048
     if case == "ties":
         x = rng.integers(0, 64, size=(rows, cols)).astype(np.float32)
+    elif case == "dup":
+        # N(0,1) on a grid: even rows on 1/256 (up to about 23 copies of a
+        # selected value), odd rows on 1/64 (about 64), so the fp32 rows'
+        # ordering buckets hold tied keys (ranked by column) and overflow into
+        # the sort network on alternate rows.
+        grid = np.where(np.arange(rows)[:, None] % 2 == 0, 256.0, 64.0)
+        x = (np.round(rng.standard_normal((rows, cols)) * grid) / grid).astype(np.float32)
     elif case == "specials":
         x = rng.standard_normal((rows, cols)).astype(np.float32)
         u = rng.random((rows, cols))
@@ -285,8 +293,11 @@ def test_block_rows_adversarial(rts, case):
         x = rng.standard_normal((rows, cols)).astype(np.float32) + np.float32(100.0)
     ends = np.full(rows, cols, np.int32)
     ends[1::7] = rng.integers(0, cols, size=len(ends[1::7]))
-    say("block adversarial", case)
-    check(rts, x, ends, k, what=f"block {case}")
+    say("block adversarial", case, dtype)
+    if dtype == "bf16":
+        check(rts, datagen.bf16_bits(x), ends, k, "bf16", what=f"block bf16 {case}")
+    else:
+        check(rts, x, ends, k, what=f"block {case}")
 
 
 def test_block_rows_strided_and_misaligned(rts):
