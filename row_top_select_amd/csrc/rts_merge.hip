@@ -973,6 +973,7 @@ __global__ __launch_bounds__(kWave) void merge_packed_wave_kernel(
 constexpr int kPairListCap = 3072;
 
 struct PairSmem {
+    static constexpr bool kWave0Find = true;
     uint32_t hist[kLevelCopies][kLevelStride];
     uint32_t bins[256];
     uint32_t red[16][4];
@@ -1113,15 +1114,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
     // Valid count and key range (every valid key is >= key32(-inf) > 0).
     // The minimum is taken over key - 1, which sends empty slots (0) to the
     // top of the unsigned range.
+    // Per-lane figures, the wave's, then lane w < world combines wave w's.
     uint32_t nv = 0, mn = 0xFFFFFFFFu, mx = 0u;
     fresh();
 #pragma unroll
     for (int q = 0; q < QK; ++q) {
-        nv += (uint32_t)__popcll(__ballot(key[q] != 0u));
+        nv += key[q] != 0u ? 1u : 0u;
         const uint32_t km1 = key[q] - 1u;
         mn = km1 < mn ? km1 : mn;
         mx = key[q] > mx ? key[q] : mx;
     }
+    nv = wave_sum32(nv);
     mn = wave_min32(mn);
     mx = wave_max32(mx);
     if (lane == 0) {
@@ -1130,13 +1133,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
         sm.red[wave][2] = mx;
     }
     lds_barrier();
-    nv = 0;
-    mn = 0xFFFFFFFFu;
-    mx = 0u;
-    for (int w = 0; w < world; ++w) {
-        nv += sm.red[w][0];
-        mn = sm.red[w][1] < mn ? sm.red[w][1] : mn;
-        mx = sm.red[w][2] > mx ? sm.red[w][2] : mx;
+    {
+        const bool wl = lane < world;
+        nv = wave_sum32(wl ? sm.red[lane][0] : 0u);
+        mn = wave_min32(wl ? sm.red[lane][1] : 0xFFFFFFFFu);
+        mx = wave_max32(wl ? sm.red[lane][2] : 0u);
     }
     mn += 1u;  // the smallest valid key (used only when there are more than k)
     int32_t* o_row = out_ids + row * (int64_t)k;
@@ -1180,11 +1181,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void 
         uint32_t c = 0;
         fresh();
 #pragma unroll
-        for (int q = 0; q < QK; ++q) c += (uint32_t)__popcll(__ballot(key[q] >= blo));
+        for (int q = 0; q < QK; ++q) c += key[q] >= blo ? 1u : 0u;
+        c = wave_sum32(c);
         if (lane == 0) sm.woff[wave] = c;
         lds_barrier();
-        uint32_t off = 0;
-        for (int w = 0; w < wave; ++w) off += sm.woff[w];
+        const uint32_t wincl = wave_incl_scan32(lane < world ? sm.woff[lane] : 0u);
+        uint32_t off = wave == 0 ? 0u : (uint32_t)__builtin_amdgcn_readlane((int)wincl, wave - 1);
         // The listed entries' gids are read back from memory (mostly cached:
         // the row was just read), a batch of registers' loads in flight
         // together rather than one round trip per register.
