@@ -300,6 +300,22 @@ def test_block_rows_adversarial(rts, case, dtype):
         check(rts, x, ends, k, what=f"block {case}")
 
 
+def test_block_rows_misaligned_bf16(rts):
+    # bf16 rows one element past an 8-byte boundary (every element read on its
+    # own), ragged row ends, k > 1024 on 8192 and 16384 columns
+    rng = np.random.default_rng(29)
+    for cols, k in ((8192, 1500), (16383, 2048)):
+        rows = 262
+        big = datagen.bf16_bits(rng.standard_normal((rows, cols + 1)).astype(np.float32))
+        xt = bf16_dev(big)[:, 1:]
+        ends = rng.integers(0, cols + 1, size=rows).astype(np.int32)
+        ends[0] = cols
+        say("block misaligned bf16", cols, k)
+        got = host(rts.topk_rows(xt, k, row_ends=dev(ends)))
+        assert_ids_equal(got, oracle.topk_rows(np.ascontiguousarray(big[:, 1:]), ends, k),
+                         f"block misaligned bf16 {cols} {k}")
+
+
 def test_block_rows_strided_and_misaligned(rts):
     # logits starting one element past a 16-byte boundary (element loads) and
     # an output wider than k (columns past k untouched)
