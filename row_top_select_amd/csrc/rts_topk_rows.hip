@@ -30,6 +30,8 @@
 //     second kernel merges them the same way.
 // The result is exact for any distribution; adversarial orders only cost more
 // compactions, never more HBM traffic.
+// Short rows with k > 1024 take a second kernel (topk_rows_block_kernel) that
+// holds a whole row in one workgroup's registers (described at the kernel).
 #include <mutex>
 #include <type_traits>
 
@@ -616,21 +618,25 @@ void topk_rows_stream_kernel(
 
 // ---------------------------------------------------------------------------
 // Short rows with a large k: one workgroup of NW waves holds the whole row in
-// registers (KPT keys per thread, the column implied by the position), so a
-// row costs one read and no compaction however many candidates survive.
-//   1. key32 of every element (0 for NaN and columns at or past the row end);
-//      valid count and [min, max] of the valid keys;
-//   2. workgroup radix levels over the keys (256 bins of the live window,
-//      lane-striped LDS histogram copies), then the tie rule at the k-th key
-//      by ascending column;
-//   3. the selected (exactly min(k, valid)) are written to LDS as composites
-//      and sorted descending by a bitonic network over the workgroup: each
-//      wave sorts 64*E in registers (even waves descending, odd ascending),
-//      then the cross-wave steps exchange through LDS and each wave finishes
-//      with an in-register merge.
-// Element i of thread t's keys: columns 4 * (g * 64 * NW + t) + j for
-// i = 4g + j, so each group of four is one 16-byte (fp32) or 8-byte (bf16)
-// load and a wave's load covers 1 KB (512 B) of the row.
+// registers (KPT elements per thread, the column implied by the position), so
+// a row costs one read and no compaction however many candidates survive.
+//   1. the row as fp32 bits (bf16 widened), an empty slot (NaN, or at or past
+//      the row end) a quiet NaN; valid count and score range;
+//   2. a first radix level linear in the score (256 bins of [min, max]),
+//      lane-striped LDS histogram copies;
+//   3. one pass: keys above the boundary bin are selected (written once the
+//      waves' offsets are known), the boundary bin's go to a per-wave LDS
+//      list, where the later levels and the tie rule (ascending column) run;
+//      a row whose list overflows runs them over its registers as keys;
+//   4. the selected (exactly min(k, valid)) in LDS are put in order: fp32 rows
+//      by bucket rank (each id written straight to its place), bf16 rows and
+//      fp32 rows with crowded buckets by a bitonic network over the workgroup
+//      (each wave sorts 64*E in registers, even waves descending, odd
+//      ascending; the cross-wave steps exchange through LDS and each wave
+//      finishes with an in-register merge).
+// Element i of thread t: column 4 * (g * 64 * NW + t) + j for i = 4g + j, so
+// each group of four is one 16-byte (fp32) or 8-byte (bf16) load and a wave's
+// load covers 1 KB (512 B) of the row.
 // ---------------------------------------------------------------------------
 template <int NW>
 struct BlockRowSmem {
