@@ -575,6 +575,27 @@ void topk_rows_stream_kernel(
         // loop head, so the stream loop waits only for the buffer it reads.
         __builtin_amdgcn_s_waitcnt(0);
     }
+    // One wave with a bf16 row of fewer than 2^16 columns sorts 32-bit words:
+    // the key's top 16 bits (the rest follow the sign) over 0xFFFF - column,
+    // the composite's order, at half the lane traffic and selects.
+    if constexpr (BF16 && P == 1) {
+        if (groups == 1 && cols <= 65536) {
+            uint32_t L32[E];
+#pragma unroll
+            for (int r = 0; r < E; ++r)
+                L32[r] = ((uint32_t)(L[r] >> 32) & 0xFFFF0000u) | ((uint32_t)L[r] & 0xFFFFu);
+            wave_bitonic_sort<E, true>(L32);
+            int lane_o = lane;
+            asm volatile("" : "+v"(lane_o));
+            int32_t* o = out + row * ld_out;
+#pragma unroll
+            for (int r = 0; r < E; ++r) {
+                const int i = lane_o * E + r;
+                if (i < k) o[i] = L32[r] ? (int32_t)(0xFFFFu - (L32[r] & 0xFFFFu)) : -1;
+            }
+            return;
+        }
+    }
     // The wave's top list, sorted descending, blocked (lane l: l*E .. l*E+E-1).
     wave_bitonic_sort<E, true>(L);
 
