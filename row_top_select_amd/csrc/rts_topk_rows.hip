@@ -124,9 +124,10 @@ __device__ __forceinline__ void radix_hist(const uint64_t (&v)[NV], uint32_t w, 
 // T such that exactly `need` nonzero entries of v[] are >= T (composites are
 // distinct).  Requires at least `need` nonzero entries, all with key >= lb
 // and low word in [id_lo, id_lo + id_span] (the piece's columns).
-template <int NV, int NS0, bool COARSE>
+template <int NV, int NS0>
 __device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[NV], int need, uint32_t lb,
-                                             uint32_t id_lo, uint32_t id_span, uint32_t* hist) {
+                                             uint32_t id_lo, uint32_t id_span, uint32_t* hist,
+                                             bool coarse) {
     uint32_t mx = 0;
 #pragma unroll
     for (int r = 0; r < NV; ++r) mx = mx > (uint32_t)(v[r] >> 32) ? mx : (uint32_t)(v[r] >> 32);
@@ -159,12 +160,13 @@ __device__ __forceinline__ uint64_t wave_kth(const uint64_t (&v)[NV], int need, 
         const uint32_t top = whi - blo, width = (1u << s) - 1u;
         span = width < top ? width : top;
         whi = w + span;
-        if (cb > (uint32_t)kWave || COARSE) {
+        if (cb > (uint32_t)kWave || coarse) {
             // A crowded bin: narrow the window to the keys actually in it.
             // All equal (ties at the k-th key): straight to the tie levels,
             // instead of levels that would count every entry into one bin.
-            // COARSE keys (bf16 widened: 2^16 apart) take this for every
-            // bin, as a bin of a few such keys is usually one key.
+            // With coarse keys (bf16 widened: 2^16 apart; a row whose last
+            // compaction ended tied) every bin takes this, as a bin of a few
+            // such keys is usually one key.
             uint32_t bmn = 0xFFFFFFFFu, bmx = 0u;
 #pragma unroll
             for (int r = 0; r < NV; ++r) {
@@ -258,6 +260,7 @@ void topk_rows_stream_kernel(
     const T* rowp = reinterpret_cast<const T*>(xv) + row * ld;
 
     int cnt = 0;                     // staged entries (wave-uniform)
+    bool coarse = BF16;              // compactions narrow every boundary bin (see wave_kth)
     int nl = 0;                      // entries in the register list L (wave-uniform)
     uint32_t thr_own = 0x007FFFFFu;  // key of -inf: every non-NaN value passes
     float f = float_of_key32(thr_own);
@@ -532,7 +535,10 @@ void topk_rows_stream_kernel(
             }
             // low words of the piece's entries: 2^32-1-col for col in [a, b)
             wave_lds_sync();  // the stage's entries are in v[]: its memory holds the histograms
-            T0 = wave_kth<E + ES, NS0, BF16>(v, k, lb, 0xFFFFFFFFu - (uint32_t)(b - 1), (uint32_t)(b - 1 - a), hist);
+            T0 = wave_kth<E + ES, NS0>(v, k, lb, 0xFFFFFFFFu - (uint32_t)(b - 1), (uint32_t)(b - 1 - a), hist,
+                                       coarse);
+            // A k-th composite with a nonzero id word ended in the tie levels.
+            coarse = BF16 || (uint32_t)T0 != 0u;
         }
         int base = 0;
         uint32_t kmin = 0xFFFFFFFFu;
